@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged decode step (KV append + decode attention) on one MI355X.
+
+A step is ``paged_kv_write`` (one new token per sequence) followed by
+``paged_attn_decode`` over every sequence of the batch, on torch's current
+stream, inputs resident in HBM.  The default workload is the high-concurrency
+batch: 256 sequences, 32 query / 8 KV heads, head_dim 128, bf16, 16-token
+blocks, lognormal context lengths (median 1024, sigma 1, clamp [1, 8192]),
+pool ~90% full with the free blocks interleaved.
+
+Output: one JSON line (rank 0).  ``value`` is decode sequences per second of the
+whole step (wall clock over the K timed steps, synchronised on both sides);
+``roofline`` prices the decode call (partition + combine kernels, timed with
+HIP events on the launch stream) against 8 TB/s with the algorithmic bytes of
+one launch: sum(ctx) * 2 * Hkv * head_dim * elem (K and V rows read once) plus
+q, out, the block-table entries and the lengths.  ``cpu_baseline`` is the fp64
+CPU oracle timed on the host cores (the same step, write + attention).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode seqs/s and achieved KV-read HBM GB/s (% of peak), 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="hc_b256",
+                   choices=["tiny", "llama8b_b64", "hc_b256", "long32k", "shared_prefix"])
+    p.add_argument("--partition-tokens", type=int, default=0)
+    p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 fast")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="HBM bytes per launch measured by rocprofv3 counters (optional)")
+    return p.parse_args(argv)
+
+
+def algorithmic_bytes(w) -> dict:
+    ctx = w.context_lens.astype(np.int64)
+    e = w.elem_bytes
+    B = w.block_size
+    kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * e
+    q = w.num_seqs * w.num_q_heads * w.head_dim * e
+    out = w.num_seqs * w.num_q_heads * w.head_dim * 4
+    tables = int(((ctx + B - 1) // B).sum()) * 4 + w.num_seqs * 4
+    return {"kv": kv, "q": q, "out": out, "tables": tables, "total": kv + q + out + tables}
+
+
+def cpu_baseline(w) -> dict:
+    import oracle
+
+    o = oracle.Oracle()
+    kc = oracle._bits(w.k_cache).copy()
+    vc = oracle._bits(w.v_cache).copy()
+    times = []
+    budget = 10.0
+    while True:
+        t0 = time.perf_counter()
+        o.kv_write(w.k_new, w.v_new, w.slot_mapping, kc, vc, w.block_size)
+        o.attn_decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, num_kv_heads=w.num_kv_heads)
+        times.append(time.perf_counter() - t0)
+        if sum(times) >= budget or len(times) >= 3:
+            break
+    med = statistics.median(times)
+    return {
+        "value": w.num_seqs / med,
+        "unit": "seqs/s",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": f"whole batch ({w.num_seqs} seqs, write + attention), median of {len(times)} runs "
+                  f"of {med:.2f} s",
+        "kv_GBps": algorithmic_bytes(w)["kv"] / med / 1e9,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   "the multi-GPU path is a design note, not a measured configuration"}))
+        return 2
+    assert torch.cuda.is_available(), "no GPU visible"
+    import paged_kv_cache_276_amd as pkv
+    from workloads import make_config
+
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    w = make_config(args.config)
+    d = {
+        "q": w.q.to(dev), "k_new": w.k_new.to(dev), "v_new": w.v_new.to(dev),
+        "k_cache": w.k_cache.to(dev), "v_cache": w.v_cache.to(dev),
+        "block_tables": torch.from_numpy(w.block_tables).to(dev),
+        "context_lens": torch.from_numpy(w.context_lens).to(dev),
+        "slot_mapping": torch.from_numpy(w.slot_mapping).to(dev),
+    }
+    plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
+                               partition_tokens=args.partition_tokens, kernel=args.kernel)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+
+    def write():
+        pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+
+    def decode():
+        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                              w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
+                              kernel=args.kernel)
+
+    print(f"[bench] warmup {args.warmup} steps, plan {plan}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        write()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    decode_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    dec_avg = statistics.mean(decode_ms)
+    nbytes = algorithmic_bytes(w)
+    achieved = nbytes["total"] / (dec_avg * 1e-3) / 1e9
+    kv_gbs = nbytes["kv"] / (dec_avg * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            t = json.load(f)
+        key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}"
+        if key in t and t[key].get("source_sha") == _kernel_source_sha():
+            traffic = t[key]["bytes_per_launch"]
+
+    rec = {
+        "metric": METRIC,
+        "value": w.num_seqs / (ms_per_step * 1e-3),
+        "unit": "seqs/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.config,
+            "num_seqs": w.num_seqs,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "context_tokens": int(w.context_lens.sum()),
+            "lengths": w.meta.get("lengths", "fixed"),
+            "kernel": plan["kernel"],
+            "partition_tokens": plan["partition_tokens"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+        },
+        "kv_read_GBps": kv_gbs,
+        "kv_read_pct_of_peak": 100.0 * kv_gbs / PEAK_HBM_GBS,
+        "decode_us": dec_avg * 1e3,
+        "decode_us_min": min(decode_ms) * 1e3,
+        "write_us": statistics.mean(write_ms) * 1e3,
+        "algorithmic_bytes": nbytes,
+        "gpu": torch.cuda.get_device_name(0),
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+    }
+
+    if not args.no_parity:
+        import oracle
+        from workloads import make_config as _mk
+
+        fresh = _mk(args.config)  # pre-write state; the GPU pool has been written K+W times (same slots)
+        ref = oracle.decode_step(fresh)
+        g = out.double().cpu().numpy()
+        err = np.abs(g - ref.out)
+        rec["parity"] = {
+            "max_err_over_allowed": float(np.max(err / (2e-3 + 1e-2 * np.abs(ref.out)))),
+            "finite": bool(np.isfinite(g).all()),
+        }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_276_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

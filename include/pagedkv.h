@@ -1,0 +1,181 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged KV-cache append and single-token
+ * decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages this library follows):
+ *  - Attention(Q,K,V) = softmax(Q K^T / sqrt(d_head)) V; at decode time each
+ *    sequence contributes one query row per head and attends over every cached
+ *    key/value of that sequence.  Page "x321.org/?p=939", section "First
+ *    understand what the KV cache is storing".
+ *  - The KV cache grows by one token per step and old K/V are reused as is:
+ *    same page and section.
+ *  - The cache of a sequence is cut into fixed-size blocks; a block table maps
+ *    each logical block to a physical block anywhere in a shared pool, and the
+ *    attention kernel follows that mapping in logical order.  Page
+ *    "x321.org/?p=939", section "PagedAttention borrows an operating-system
+ *    trick"; page "chenhuiyu.github.io/blog/llm-infra-vllm-en", sections "Why
+ *    naive KV allocation wastes memory" and "Logical continuity, physical
+ *    flexibility".
+ *  - Blocks holding an identical prefix may be named by several block tables;
+ *    page "praveentn.live/architecture/quiz/pagedattention-kv-cache-constraint",
+ *    section "What the change bought".  Reads through shared blocks are
+ *    supported; copying a shared block before writing into it is the caller's
+ *    job.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are HIP device pointers, (host) are host
+ *    pointers.  Every array is dense and row-major as documented.  The caller
+ *    owns all memory; the library allocates nothing and keeps no pointer after
+ *    a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; the caller keeps the buffers alive until the stream
+ *    has passed the enqueued work.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error nothing is enqueued (all-or-nothing).  No C++ exception crosses the
+ *    ABI.
+ *  - Device-side contents are not validated on the host, but the kernels stay
+ *    inside the buffers whatever those contents are: an out-of-range slot is
+ *    not written; an out-of-range block-table entry or context length turns
+ *    the affected output rows into NaN.
+ *  - Layouts.  Cache pools K and V: [num_blocks][num_kv_heads][block_size]
+ *    [head_dim] of `dtype`.  A slot number is physical_block * block_size +
+ *    offset.  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+    PKV_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+    PKV_ERR_DTYPE = 3,       /* unknown element type */
+    PKV_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this head_dim / block_size / group size */
+    PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than paged_attn_workspace_bytes */
+    PKV_ERR_HIP = 6,         /* the HIP runtime reported an error while enqueueing */
+    PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0, /* IEEE binary32 */
+    PKV_BF16 = 1 /* bfloat16 (upper half of a binary32) */
+} pkv_dtype;
+
+/* Shape of the K and V pools (host struct).  Supported: head_dim 64, 128 or
+ * 256; block_size 8, 16, 32 or 64; dtype PKV_F32 or PKV_BF16;
+ * num_blocks * block_size < 2^31. */
+typedef struct pkv_cache_desc {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype; /* a pkv_dtype */
+} pkv_cache_desc;
+
+/* Kernel families of paged_attn_decode. */
+#define PKV_KERNEL_AUTO 0    /* library choice */
+#define PKV_KERNEL_GENERIC 1 /* any supported shape and dtype */
+#define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 16 or 32, group size 1, 2, 4 or 8 */
+
+/* Optional decode settings (host struct; NULL = all defaults). */
+typedef struct pkv_decode_opts {
+    int32_t partition_tokens; /* 0 = library choice; else tokens per split-K partition, a multiple of 64 */
+    int32_t kernel;           /* a PKV_KERNEL_* value */
+} pkv_decode_opts;
+
+/* What paged_attn_decode will launch for a given shape (host struct). */
+typedef struct pkv_decode_plan {
+    int32_t kernel;           /* PKV_KERNEL_GENERIC or PKV_KERNEL_FAST */
+    int32_t partition_tokens; /* tokens per partition */
+    int32_t max_partitions;   /* ceil(max_blocks_per_seq * block_size / partition_tokens) */
+    int32_t threads_per_block;
+    int64_t grid_blocks;      /* workgroups of the partition kernel */
+    uint64_t workspace_bytes; /* required workspace (0 when no sequence can span two partitions) */
+} pkv_decode_plan;
+
+/*
+ * paged_kv_write -- append step: store each new token's key and value rows in
+ * its slot (page "x321.org/?p=939", section "First understand what the KV
+ * cache is storing": the cache grows as tokens are produced).
+ *
+ *   k_new, v_new  (device) [num_tokens][num_kv_heads][head_dim] of cache->dtype
+ *   slot_mapping  (device) int32 [num_tokens]; slot s goes to block s / block_size,
+ *                 offset s % block_size; s < 0 = skip this token; s >= num_blocks *
+ *                 block_size is not written
+ *   k_cache, v_cache (device) pools as described above, updated in place
+ *   cache         (host) pool shape
+ *
+ * The copy is bit-exact (NaN payloads, -0.0 and subnormals arrive unchanged).
+ * Two tokens with the same slot race; the result is then unspecified.
+ * num_tokens == 0 enqueues nothing and returns PKV_OK.
+ */
+pkv_status paged_kv_write(const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                          int32_t num_tokens, void *k_cache, void *v_cache,
+                          const pkv_cache_desc *cache, void *stream);
+
+/*
+ * paged_attn_plan -- host-only: which kernel, partition size, grid and
+ * workspace size paged_attn_decode uses for these sizes.  Touches no device.
+ */
+pkv_status paged_attn_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                           const pkv_cache_desc *cache, const pkv_decode_opts *opts,
+                           pkv_decode_plan *plan);
+
+/* paged_attn_workspace_bytes -- host-only: plan->workspace_bytes of paged_attn_plan. */
+pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t max_blocks_per_seq, const pkv_cache_desc *cache,
+                                      const pkv_decode_opts *opts, uint64_t *bytes);
+
+/*
+ * paged_attn_decode -- single-token decode attention over paged K/V:
+ * out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i, where K_i, V_i are the
+ * context_lens[i] tokens of sequence i, token j read from physical block
+ * block_tables[i][j / block_size] at offset j % block_size, KV head
+ * h / (num_q_heads / num_kv_heads)  (page "x321.org/?p=939", sections "First
+ * understand what the KV cache is storing" and "PagedAttention borrows an
+ * operating-system trick").
+ *
+ *   q             (device) [num_seqs][num_q_heads][head_dim] of cache->dtype
+ *   k_cache, v_cache (device) pools
+ *   block_tables  (device) int32 [num_seqs][max_blocks_per_seq]; only the first
+ *                 ceil(context_lens[i] / block_size) entries of row i are read;
+ *                 rows may name the same physical blocks (shared prefixes)
+ *   context_lens  (device) int32 [num_seqs]; tokens of each sequence, including
+ *                 the one appended this step; 0 gives an all-zero output row
+ *   scale         softmax scale (normally 1/sqrt(head_dim))
+ *   out           (device) fp32 [num_seqs][num_q_heads][head_dim]
+ *   workspace     (device) scratch of at least paged_attn_workspace_bytes bytes,
+ *                 16-byte aligned; may be NULL when that size is 0.  Its
+ *                 contents need no initialisation and are garbage afterwards.
+ *   opts          (host) NULL or settings
+ *
+ * Long contexts are cut into partitions of plan.partition_tokens tokens; each
+ * partition yields a running max, a softmax denominator and an unnormalised
+ * output, merged by a log-sum-exp combine.  Results do not depend on the
+ * physical placement of blocks (the summation order is fixed by logical token
+ * positions).  Calls that share a workspace must be serialised on one stream.
+ */
+pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float scale, float *out, void *workspace, uint64_t workspace_bytes,
+                             const pkv_cache_desc *cache, const pkv_decode_opts *opts,
+                             void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *pkv_status_string(pkv_status status);
+
+/* Library version string (static). */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -81,9 +81,14 @@ class Oracle:
         i32, vp = ctypes.c_int32, ctypes.c_void_p
         self.lib.oracle_kv_write.restype = ctypes.c_int
         self.lib.oracle_kv_write.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32]
+        self.lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib.oracle_num_threads.argtypes = []
         self.lib.oracle_attn_decode.restype = ctypes.c_int
         self.lib.oracle_attn_decode.argtypes = [
             vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, i32, vp]
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
 
     @staticmethod
     def _check(rc: int) -> None:

@@ -36,6 +36,9 @@
  * 16 bits of a binary32).  Every stored value is widened to fp64 exactly.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -230,4 +233,14 @@ int oracle_attn_decode(const void *q, const void *k_cache, const void *v_cache,
         }
     }
     return err;
+}
+
+/* Host threads the row loop above may use (reported beside CPU timings). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

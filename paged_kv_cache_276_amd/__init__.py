@@ -1,0 +1,191 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+Thin binding over the C ABI of ``libpagedkv.so`` (``include/pagedkv.h``).  The
+functions carry the C entry points' names and only marshal arguments: shape and
+dtype checks, pointers, the current HIP stream, and a cached workspace buffer.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback.
+
+    paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache)
+    out = paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale)
+
+Layouts: pools ``[num_blocks][num_kv_heads][block_size][head_dim]`` (fp32 or
+bf16); ``q`` ``[num_seqs][num_q_heads][head_dim]`` of the pool dtype;
+``block_tables`` int32 ``[num_seqs][max_blocks_per_seq]``; ``context_lens`` and
+``slot_mapping`` int32; ``out`` fp32 ``[num_seqs][num_q_heads][head_dim]``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    KERNEL_NAMES,
+    PKV_KERNEL_AUTO,
+    PKV_KERNEL_FAST,
+    PKV_KERNEL_GENERIC,
+    CacheDesc,
+    DecodeOpts,
+    DecodePlan,
+    PkvError,
+)
+
+__all__ = [
+    "paged_kv_write",
+    "paged_attn_decode",
+    "paged_attn_plan",
+    "paged_attn_workspace_bytes",
+    "cache_desc",
+    "version",
+    "PkvError",
+]
+
+_DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
+
+
+def version() -> str:
+    return _lib.lib().pkv_version().decode()
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be [num_blocks][num_kv_heads][block_size][head_dim]")
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    nb, hkv, b, d = k_cache.shape
+    return CacheDesc(nb, b, hkv, d, _DTYPES[k_cache.dtype])
+
+
+def _opts(partition_tokens: int, kernel: int) -> DecodeOpts:
+    return DecodeOpts(int(partition_tokens), int(kernel))
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t: torch.Tensor, name: str, device: torch.device) -> None:
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def paged_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Store token t's K/V rows at slot slot_mapping[t] (negative = skip), bit-exact, in place."""
+    dev = k_cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n, dev)
+    desc = cache_desc(k_cache)
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache/v_cache differ")
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1, "slot_mapping must be int32 [T]")
+    T = slot_mapping.shape[0]
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t.dtype == k_cache.dtype, f"{n} dtype must match the cache")
+        _need(tuple(t.shape) == (T, desc.num_kv_heads, desc.head_dim), f"{n} must be [T][Hkv][D]")
+    st = _lib.lib().paged_kv_write(
+        ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+        ctypes.c_void_p(slot_mapping.data_ptr()), T, ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.byref(desc), _stream(dev, stream))
+    _lib.check(st, "paged_kv_write")
+
+
+def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
+                    partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO) -> Dict[str, int]:
+    """Host-only launch plan (kernel family, partition size, grid, workspace bytes)."""
+    desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
+    plan = DecodePlan()
+    st = _lib.lib().paged_attn_plan(num_seqs, num_q_heads, max_blocks_per_seq, ctypes.byref(desc),
+                                    ctypes.byref(_opts(partition_tokens, kernel)), ctypes.byref(plan))
+    _lib.check(st, "paged_attn_plan")
+    return {
+        "kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)),
+        "partition_tokens": plan.partition_tokens,
+        "max_partitions": plan.max_partitions,
+        "threads_per_block": plan.threads_per_block,
+        "grid_blocks": plan.grid_blocks,
+        "workspace_bytes": plan.workspace_bytes,
+    }
+
+
+def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
+                               partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO) -> int:
+    desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
+    out = ctypes.c_uint64(0)
+    st = _lib.lib().paged_attn_workspace_bytes(num_seqs, num_q_heads, max_blocks_per_seq,
+                                               ctypes.byref(desc),
+                                               ctypes.byref(_opts(partition_tokens, kernel)),
+                                               ctypes.byref(out))
+    _lib.check(st, "paged_attn_workspace_bytes")
+    return int(out.value)
+
+
+_workspaces: Dict[Tuple[torch.device, int], torch.Tensor] = {}
+
+
+def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
+                      stream=None) -> torch.Tensor:
+    """out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i over the paged K/V of sequence i (fp32)."""
+    dev = k_cache.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _dev(t, n, dev)
+    desc = cache_desc(k_cache)
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache/v_cache differ")
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim and q.dtype == k_cache.dtype,
+          "q must be [S][Hq][D] of the cache dtype")
+    S, Hq = q.shape[0], q.shape[1]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be int32 [S][max_blocks_per_seq]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty((S, Hq, desc.head_dim), dtype=torch.float32, device=dev)
+    _dev(out, "out", dev)
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
+    maxb = block_tables.shape[1]
+    opts = _opts(partition_tokens, kernel)
+    s = _stream(dev, stream)
+    need = paged_attn_workspace_bytes(S, Hq, maxb, desc, partition_tokens, kernel)
+    if workspace is None:
+        workspace = _workspace(dev, int(s.value or 0), need)
+    elif need:
+        _dev(workspace, "workspace", dev)
+        _need(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.lib().paged_attn_decode(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()), maxb,
+        ctypes.c_void_p(context_lens.data_ptr()), S, Hq, ctypes.c_float(scale),
+        ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes, ctypes.byref(desc), ctypes.byref(opts), s)
+    _lib.check(st, "paged_attn_decode")
+    return out

@@ -1,0 +1,187 @@
+// api.hip -- the extern "C" entry points of libpagedkv.so (declared in
+// include/pagedkv.h).  Host code only: argument validation, the launch plan,
+// and dispatch to the kernels.  Every check runs before anything is enqueued.
+#include <stdint.h>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+#define PKV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int32_t kDefaultPartitionTokens = 512;
+
+bool is_pow2_in(int32_t v, int32_t lo, int32_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkv_status check_desc(const pkv_cache_desc* c) {
+    if (!c) return PKV_ERR_NULL;
+    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+        return PKV_ERR_SHAPE;
+    if (!is_pow2_in(c->block_size, 8, 64)) return PKV_ERR_UNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)c->num_blocks * c->block_size > INT32_MAX) return PKV_ERR_SHAPE;
+    return PKV_OK;
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+struct WorkspaceLayout {
+    uint64_t ml_bytes;   // float2 [S][Hq][P]
+    uint64_t acc_bytes;  // float  [S][Hq][P][D]
+    uint64_t total;
+};
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_parts,
+                                 int32_t head_dim) {
+    WorkspaceLayout w{0, 0, 0};
+    if (max_parts <= 1) return w;
+    const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_parts;
+    w.ml_bytes = align_up(rows * sizeof(float2), 256);
+    w.acc_bytes = rows * (uint64_t)head_dim * sizeof(float);
+    w.total = w.ml_bytes + w.acc_bytes;
+    return w;
+}
+
+pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                     const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                     pkv_decode_plan* plan) {
+    pkv_status st = check_desc(cache);
+    if (st != PKV_OK) return st;
+    if (!plan) return PKV_ERR_NULL;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_SHAPE;
+    if (num_q_heads % cache->num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+    const int32_t group = num_q_heads / cache->num_kv_heads;
+
+    int32_t kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
+    const bool fast_ok = pkv::fast_supports(cache->dtype, cache->head_dim, cache->block_size, group);
+    const bool generic_ok = pkv::generic_supports(cache->dtype, cache->head_dim, group);
+    if (kernel == PKV_KERNEL_AUTO) {
+        kernel = fast_ok ? PKV_KERNEL_FAST : PKV_KERNEL_GENERIC;
+    }
+    if (kernel == PKV_KERNEL_FAST && !fast_ok) return PKV_ERR_UNSUPPORTED;
+    if (kernel == PKV_KERNEL_GENERIC && !generic_ok) return PKV_ERR_UNSUPPORTED;
+    if (kernel != PKV_KERNEL_FAST && kernel != PKV_KERNEL_GENERIC) return PKV_ERR_UNSUPPORTED;
+
+    int32_t part = opts && opts->partition_tokens ? opts->partition_tokens : kDefaultPartitionTokens;
+    if (part <= 0 || part % 64 != 0) return PKV_ERR_SHAPE;
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * cache->block_size;
+    const int64_t max_parts = (table_tokens + part - 1) / part;
+    const int64_t grid = max_parts * cache->num_kv_heads * (int64_t)num_seqs;
+    if (grid > INT32_MAX || (int64_t)num_seqs * num_q_heads > INT32_MAX) return PKV_ERR_SHAPE;
+
+    plan->kernel = kernel;
+    plan->partition_tokens = part;
+    plan->max_partitions = (int32_t)max_parts;
+    plan->threads_per_block = 64;
+    plan->grid_blocks = grid;
+    plan->workspace_bytes = workspace_layout(num_seqs, num_q_heads, (int32_t)max_parts, cache->head_dim).total;
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_API pkv_status paged_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  int32_t num_tokens, void* k_cache, void* v_cache,
+                                  const pkv_cache_desc* cache, void* stream) {
+    pkv_status st = check_desc(cache);
+    if (st != PKV_OK) return st;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (!k_cache || !v_cache) return PKV_ERR_NULL;
+    if (num_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return PKV_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+        return PKV_ERR_ALIGN;
+    if (num_tokens == 0) return PKV_OK;
+    const int32_t elem = cache->dtype == PKV_F32 ? 4 : 2;
+    const hipError_t e = pkv::launch_kv_write(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+                                              cache->num_blocks, cache->block_size, cache->num_kv_heads,
+                                              cache->head_dim * elem, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_API pkv_status paged_attn_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                   const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                                   pkv_decode_plan* plan) {
+    return make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, plan);
+}
+
+PKV_API pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                              const pkv_decode_opts* opts, uint64_t* bytes) {
+    if (!bytes) return PKV_ERR_NULL;
+    pkv_decode_plan plan;
+    const pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, &plan);
+    if (st != PKV_OK) return st;
+    *bytes = plan.workspace_bytes;
+    return PKV_OK;
+}
+
+PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     float scale, float* out, void* workspace, uint64_t workspace_bytes,
+                                     const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                                     void* stream) {
+    pkv_decode_plan plan;
+    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, &plan);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return PKV_ERR_ALIGN;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace) return PKV_ERR_WORKSPACE;
+        if (workspace_bytes < plan.workspace_bytes) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    }
+
+    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, plan.max_partitions, cache->head_dim);
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_blocks = cache->num_blocks;
+    a.block_size = cache->block_size;
+    a.head_dim = cache->head_dim;
+    a.dtype = cache->dtype;
+    a.scale = scale;
+    a.out = out;
+    a.ws_ml = wl.total ? static_cast<float2*>(workspace) : nullptr;
+    a.ws_acc = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_bytes) : nullptr;
+    a.part_tokens = plan.partition_tokens;
+    a.max_parts = plan.max_partitions;
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = plan.kernel == PKV_KERNEL_FAST ? pkv::launch_decode_fast(a, s)
+                                                   : pkv::launch_decode_generic(a, s);
+    if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+PKV_API const char* pkv_status_string(pkv_status status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "invalid or inconsistent size";
+        case PKV_ERR_DTYPE: return "unknown element type";
+        case PKV_ERR_UNSUPPORTED: return "no kernel for this shape";
+        case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PKV_ERR_HIP: return "HIP runtime error while enqueueing";
+        case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+PKV_API const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }

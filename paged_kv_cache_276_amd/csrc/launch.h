@@ -1,0 +1,47 @@
+// launch.h -- host-side launchers of the libpagedkv kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Arguments of one decode call after host validation.  Workspace: ws_ml holds
+// (running max in log2 units, softmax denominator) per [seq][q_head][partition];
+// ws_acc the unnormalised output per [seq][q_head][partition][head_dim].
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t head_dim;
+    int32_t dtype;  // pkv_dtype
+    float scale;
+    float* out;
+    float* ws_acc;
+    float2* ws_ml;
+    int32_t part_tokens;
+    int32_t max_parts;
+};
+
+hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                           int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t row_bytes,
+                           hipStream_t stream);
+
+// Returns hipErrorInvalidValue when no instantiation matches the shape.
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+
+bool generic_supports(int32_t dtype, int32_t head_dim, int32_t group);
+bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
+
+}  // namespace pkv
