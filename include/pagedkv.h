@@ -81,22 +81,30 @@ typedef struct pkv_cache_desc {
 /* Kernel families of paged_attn_decode. */
 #define PKV_KERNEL_AUTO 0    /* library choice */
 #define PKV_KERNEL_GENERIC 1 /* any supported shape and dtype */
-#define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 16 or 32, group size 1, 2, 4 or 8 */
+#define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 16, 32 or 64, group size 1, 2, 4 or 8 */
 
 /* Optional decode settings (host struct; NULL = all defaults). */
 typedef struct pkv_decode_opts {
-    int32_t partition_tokens; /* 0 = library choice; else tokens per split-K partition, a multiple of 64 */
+    int32_t partition_tokens; /* generic kernel: tokens per split-K partition, a multiple of 64;
+                                 0 = library choice */
     int32_t kernel;           /* a PKV_KERNEL_* value */
+    int32_t grid_waves;       /* fast kernel: number of waves that share the work, 1 ..
+                                 PKV_MAX_GRID_WAVES; 0 = as many as the device keeps resident */
 } pkv_decode_opts;
+
+/* Upper bound of the fast kernel's wave count (sizes its workspace). */
+#define PKV_MAX_GRID_WAVES 8192
 
 /* What paged_attn_decode will launch for a given shape (host struct). */
 typedef struct pkv_decode_plan {
     int32_t kernel;           /* PKV_KERNEL_GENERIC or PKV_KERNEL_FAST */
-    int32_t partition_tokens; /* tokens per partition */
-    int32_t max_partitions;   /* ceil(max_blocks_per_seq * block_size / partition_tokens) */
+    int32_t partition_tokens; /* generic: tokens per partition; fast: 16 (tokens per work tile) */
+    int32_t max_partitions;   /* generic: ceil(max_blocks_per_seq * block_size / partition_tokens);
+                                 fast: most partial results one (sequence, KV head) can leave */
     int32_t threads_per_block;
-    int64_t grid_blocks;      /* workgroups of the partition kernel */
-    uint64_t workspace_bytes; /* required workspace (0 when no sequence can span two partitions) */
+    int64_t grid_blocks;      /* generic: workgroups of the partition kernel; fast: the requested
+                                 wave count, or 0 when the device decides (resident waves) */
+    uint64_t workspace_bytes; /* required workspace (0 when nothing needs merging) */
 } pkv_decode_plan;
 
 /*
@@ -155,11 +163,15 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 contents need no initialisation and are garbage afterwards.
  *   opts          (host) NULL or settings
  *
- * Long contexts are cut into partitions of plan.partition_tokens tokens; each
- * partition yields a running max, a softmax denominator and an unnormalised
- * output, merged by a log-sum-exp combine.  Results do not depend on the
- * physical placement of blocks (the summation order is fixed by logical token
- * positions).  Calls that share a workspace must be serialised on one stream.
+ * Work splitting.  The generic kernel cuts every sequence into partitions of
+ * plan.partition_tokens tokens.  The fast kernel lays all (sequence, KV head,
+ * 16-token tile) triples end to end and gives each wave of its grid an equal
+ * contiguous run of tiles, so a long sequence spreads over several waves and
+ * many short ones share a wave.  Either way every piece yields a running max,
+ * a softmax denominator and an unnormalised output, merged by a log-sum-exp
+ * combine.  Results do not depend on the physical placement of blocks (the
+ * summation order is fixed by logical token positions and the wave count).
+ * Calls that share a workspace must be serialised on one stream.
  */
 pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -60,8 +60,8 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(nb, b, hkv, d, _DTYPES[k_cache.dtype])
 
 
-def _opts(partition_tokens: int, kernel: int) -> DecodeOpts:
-    return DecodeOpts(int(partition_tokens), int(kernel))
+def _opts(partition_tokens: int, kernel: int, grid_waves: int = 0) -> DecodeOpts:
+    return DecodeOpts(int(partition_tokens), int(kernel), int(grid_waves))
 
 
 def _need(cond: bool, msg: str) -> None:
@@ -105,12 +105,14 @@ def paged_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch
 
 
 def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
-                    partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO) -> Dict[str, int]:
+                    partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
+                    grid_waves: int = 0) -> Dict[str, int]:
     """Host-only launch plan (kernel family, partition size, grid, workspace bytes)."""
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     plan = DecodePlan()
     st = _lib.lib().paged_attn_plan(num_seqs, num_q_heads, max_blocks_per_seq, ctypes.byref(desc),
-                                    ctypes.byref(_opts(partition_tokens, kernel)), ctypes.byref(plan))
+                                    ctypes.byref(_opts(partition_tokens, kernel, grid_waves)),
+                                    ctypes.byref(plan))
     _lib.check(st, "paged_attn_plan")
     return {
         "kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)),
@@ -123,12 +125,13 @@ def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, ca
 
 
 def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
-                               partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO) -> int:
+                               partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
+                               grid_waves: int = 0) -> int:
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     out = ctypes.c_uint64(0)
     st = _lib.lib().paged_attn_workspace_bytes(num_seqs, num_q_heads, max_blocks_per_seq,
                                                ctypes.byref(desc),
-                                               ctypes.byref(_opts(partition_tokens, kernel)),
+                                               ctypes.byref(_opts(partition_tokens, kernel, grid_waves)),
                                                ctypes.byref(out))
     _lib.check(st, "paged_attn_workspace_bytes")
     return int(out.value)
@@ -152,7 +155,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                       partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
-                      stream=None) -> torch.Tensor:
+                      grid_waves: int = 0, stream=None) -> torch.Tensor:
     """out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i over the paged K/V of sequence i (fp32)."""
     dev = k_cache.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
@@ -172,9 +175,9 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _dev(out, "out", dev)
     _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
     maxb = block_tables.shape[1]
-    opts = _opts(partition_tokens, kernel)
+    opts = _opts(partition_tokens, kernel, grid_waves)
     s = _stream(dev, stream)
-    need = paged_attn_workspace_bytes(S, Hq, maxb, desc, partition_tokens, kernel)
+    need = paged_attn_workspace_bytes(S, Hq, maxb, desc, partition_tokens, kernel, grid_waves)
     if workspace is None:
         workspace = _workspace(dev, int(s.value or 0), need)
     elif need:

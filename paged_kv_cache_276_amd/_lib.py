@@ -41,7 +41,8 @@ class CacheDesc(ctypes.Structure):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("grid_waves", ctypes.c_int32)]
 
 
 class DecodePlan(ctypes.Structure):

@@ -32,19 +32,34 @@ pkv_status check_desc(const pkv_cache_desc* c) {
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-    uint64_t ml_bytes;   // float2 [S][Hq][P]
-    uint64_t acc_bytes;  // float  [S][Hq][P][D]
+    uint64_t rec_bytes;  // fast: int2 [S][Hkv]
+    uint64_t ml_bytes;   // generic: float2 [S][Hq][P]; fast: float2 [slots][G]
+    uint64_t acc_bytes;  // generic: float [S][Hq][P][D]; fast: float [slots][G][D]
     uint64_t total;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_parts,
-                                 int32_t head_dim) {
-    WorkspaceLayout w{0, 0, 0};
+// Generic kernel: one partial per (sequence, query head, partition).
+WorkspaceLayout generic_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_parts,
+                               int32_t head_dim) {
+    WorkspaceLayout w{0, 0, 0, 0};
     if (max_parts <= 1) return w;
     const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_parts;
     w.ml_bytes = align_up(rows * sizeof(float2), 256);
     w.acc_bytes = rows * (uint64_t)head_dim * sizeof(float);
     w.total = w.ml_bytes + w.acc_bytes;
+    return w;
+}
+
+// Fast kernel: partial slot u + w for unit u = seq * Hkv + kv_head met by wave w;
+// at most (units + waves) slots, each holding the unit's G query heads.
+WorkspaceLayout fast_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim) {
+    WorkspaceLayout w{0, 0, 0, 0};
+    const uint64_t units = (uint64_t)num_seqs * (uint64_t)num_kv_heads;
+    const uint64_t slots = units + (uint64_t)pkv::kMaxGridWaves;
+    w.rec_bytes = align_up(units * sizeof(int2), 256);
+    w.ml_bytes = align_up(slots * (uint64_t)group * sizeof(float2), 256);
+    w.acc_bytes = slots * (uint64_t)group * (uint64_t)head_dim * sizeof(float);
+    w.total = w.rec_bytes + w.ml_bytes + w.acc_bytes;
     return w;
 }
 
@@ -59,8 +74,12 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
     if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / cache->num_kv_heads;
 
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * cache->block_size;
+    // the fast kernel indexes 16-token tiles of all (sequence, KV head) pairs with int32
+    const int64_t fast_tiles = (int64_t)num_seqs * ((table_tokens + 15) / 16) * cache->num_kv_heads;
     int32_t kernel = opts ? opts->kernel : PKV_KERNEL_AUTO;
-    const bool fast_ok = pkv::fast_supports(cache->dtype, cache->head_dim, cache->block_size, group);
+    const bool fast_ok = pkv::fast_supports(cache->dtype, cache->head_dim, cache->block_size, group) &&
+                         fast_tiles < INT32_MAX;
     const bool generic_ok = pkv::generic_supports(cache->dtype, cache->head_dim, group);
     if (kernel == PKV_KERNEL_AUTO) {
         kernel = fast_ok ? PKV_KERNEL_FAST : PKV_KERNEL_GENERIC;
@@ -68,20 +87,33 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
     if (kernel == PKV_KERNEL_FAST && !fast_ok) return PKV_ERR_UNSUPPORTED;
     if (kernel == PKV_KERNEL_GENERIC && !generic_ok) return PKV_ERR_UNSUPPORTED;
     if (kernel != PKV_KERNEL_FAST && kernel != PKV_KERNEL_GENERIC) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * num_q_heads > INT32_MAX) return PKV_ERR_SHAPE;
+
+    const int32_t waves = opts ? opts->grid_waves : 0;
+    if (waves < 0 || waves > pkv::kMaxGridWaves) return PKV_ERR_SHAPE;
+
+    if (kernel == PKV_KERNEL_FAST) {
+        plan->kernel = kernel;
+        plan->partition_tokens = 16;
+        plan->max_partitions = pkv::kMaxGridWaves;
+        plan->threads_per_block = 64;
+        plan->grid_blocks = waves;
+        plan->workspace_bytes = fast_layout(num_seqs, cache->num_kv_heads, group, cache->head_dim).total;
+        return PKV_OK;
+    }
 
     int32_t part = opts && opts->partition_tokens ? opts->partition_tokens : kDefaultPartitionTokens;
     if (part <= 0 || part % 64 != 0) return PKV_ERR_SHAPE;
-    const int64_t table_tokens = (int64_t)max_blocks_per_seq * cache->block_size;
     const int64_t max_parts = (table_tokens + part - 1) / part;
     const int64_t grid = max_parts * cache->num_kv_heads * (int64_t)num_seqs;
-    if (grid > INT32_MAX || (int64_t)num_seqs * num_q_heads > INT32_MAX) return PKV_ERR_SHAPE;
+    if (grid > INT32_MAX) return PKV_ERR_SHAPE;
 
     plan->kernel = kernel;
     plan->partition_tokens = part;
     plan->max_partitions = (int32_t)max_parts;
     plan->threads_per_block = 64;
     plan->grid_blocks = grid;
-    plan->workspace_bytes = workspace_layout(num_seqs, num_q_heads, (int32_t)max_parts, cache->head_dim).total;
+    plan->workspace_bytes = generic_layout(num_seqs, num_q_heads, (int32_t)max_parts, cache->head_dim).total;
     return PKV_OK;
 }
 
@@ -141,7 +173,11 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
     }
 
-    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, plan.max_partitions, cache->head_dim);
+    const int32_t group = num_q_heads / cache->num_kv_heads;
+    const WorkspaceLayout wl =
+        plan.kernel == PKV_KERNEL_FAST ? fast_layout(num_seqs, cache->num_kv_heads, group, cache->head_dim)
+                                       : generic_layout(num_seqs, num_q_heads, plan.max_partitions, cache->head_dim);
+    char* ws = static_cast<char*>(workspace);
     pkv::DecodeArgs a;
     a.q = q;
     a.k_cache = k_cache;
@@ -158,15 +194,21 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
     a.dtype = cache->dtype;
     a.scale = scale;
     a.out = out;
-    a.ws_ml = wl.total ? static_cast<float2*>(workspace) : nullptr;
-    a.ws_acc = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_bytes) : nullptr;
+    a.ws_rec = wl.total ? reinterpret_cast<int2*>(ws) : nullptr;
+    a.ws_ml = wl.total ? reinterpret_cast<float2*>(ws + wl.rec_bytes) : nullptr;
+    a.ws_acc = wl.total ? reinterpret_cast<float*>(ws + wl.rec_bytes + wl.ml_bytes) : nullptr;
     a.part_tokens = plan.partition_tokens;
     a.max_parts = plan.max_partitions;
+    a.grid_waves = opts ? opts->grid_waves : 0;
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = plan.kernel == PKV_KERNEL_FAST ? pkv::launch_decode_fast(a, s)
-                                                   : pkv::launch_decode_generic(a, s);
-    if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
+    hipError_t e;
+    if (plan.kernel == PKV_KERNEL_FAST) {
+        e = pkv::launch_decode_fast(a, s);  // partition kernel + merge
+    } else {
+        e = pkv::launch_decode_generic(a, s);
+        if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
+    }
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

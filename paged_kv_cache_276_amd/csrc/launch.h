@@ -27,9 +27,13 @@ struct DecodeArgs {
     float* out;
     float* ws_acc;
     float2* ws_ml;
+    int2* ws_rec;  // fast kernel: per (seq, kv head) first partial slot and partial count
     int32_t part_tokens;
     int32_t max_parts;
+    int32_t grid_waves;  // fast kernel: requested waves (0 = resident capacity)
 };
+
+constexpr int32_t kMaxGridWaves = 8192;  // PKV_MAX_GRID_WAVES
 
 hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                            int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_blocks,
@@ -40,6 +44,7 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine_fast(const DecodeArgs& a, hipStream_t stream);
 
 bool generic_supports(int32_t dtype, int32_t head_dim, int32_t group);
 bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

@@ -58,18 +58,18 @@ def _desc(nb=64, b=16, hkv=8, d=128, dtype=1):
     return CacheDesc(nb, b, hkv, d, dtype)
 
 
-def _plan(L, S, hq, maxb, desc, part=0, kernel=0):
+def _plan(L, S, hq, maxb, desc, part=0, kernel=0, waves=0):
     from paged_kv_cache_276_amd import DecodeOpts, DecodePlan
 
     plan = DecodePlan()
-    st = L.paged_attn_plan(S, hq, maxb, ctypes.byref(desc), ctypes.byref(DecodeOpts(part, kernel)),
+    st = L.paged_attn_plan(S, hq, maxb, ctypes.byref(desc), ctypes.byref(DecodeOpts(part, kernel, waves)),
                            ctypes.byref(plan))
     return st, plan
 
 
 def test_plan_workspace_and_grid(L):
-    st, plan = _plan(L, 256, 32, 512, _desc(nb=30000))
-    assert st == 0
+    st, plan = _plan(L, 256, 32, 512, _desc(nb=30000), kernel=1)
+    assert st == 0 and plan.kernel == 1
     assert plan.partition_tokens % 64 == 0
     assert plan.max_partitions == -(-512 * 16 // plan.partition_tokens)
     assert plan.grid_blocks == plan.max_partitions * 8 * 256
@@ -83,10 +83,29 @@ def test_plan_workspace_and_grid(L):
     from paged_kv_cache_276_amd import DecodeOpts
 
     d = _desc(nb=30000)
-    assert L.paged_attn_workspace_bytes(256, 32, 512, ctypes.byref(d), ctypes.byref(DecodeOpts(256, 0)),
+    assert L.paged_attn_workspace_bytes(256, 32, 512, ctypes.byref(d), ctypes.byref(DecodeOpts(256, 1, 0)),
                                         ctypes.byref(out)) == 0
-    st, plan = _plan(L, 256, 32, 512, d, part=256)
+    st, plan = _plan(L, 256, 32, 512, d, part=256, kernel=1)
     assert out.value == plan.workspace_bytes
+
+
+def test_plan_fast_kernel(L):
+    """bf16, head_dim 128, block 16/32/64, groups 1/2/4/8 select the fast kernel by default."""
+    for b in (16, 32, 64):
+        for g in (1, 2, 4, 8):
+            st, plan = _plan(L, 256, 8 * g, 64, _desc(nb=30000, b=b))
+            assert st == 0 and plan.kernel == 2, (b, g)
+            units, slots = 256 * 8, 256 * 8 + 8192
+            assert plan.workspace_bytes >= units * 8 + slots * g * (128 * 4 + 8)
+    for desc, hq in ((_desc(b=8), 32), (_desc(d=64), 32), (_desc(dtype=0), 32), (_desc(), 128)):
+        st, plan = _plan(L, 4, hq, 16, desc)
+        assert st == 0 and plan.kernel == 1
+        st, plan = _plan(L, 4, hq, 16, desc, kernel=2)
+        assert st == 4
+    st, plan = _plan(L, 4, 32, 16, _desc(), waves=100)
+    assert st == 0 and plan.grid_blocks == 100
+    assert _plan(L, 4, 32, 16, _desc(), waves=8193)[0] == 2
+    assert _plan(L, 4, 32, 16, _desc(), waves=-1)[0] == 2
 
 
 @pytest.mark.parametrize(
@@ -102,7 +121,7 @@ def test_plan_workspace_and_grid(L):
         (dict(hq=8 * 3), 4),                    # group of 3: no kernel
         (dict(S=-1), 2),
         (dict(maxb=0), 2),
-        (dict(part=100), 2),                    # partition not a multiple of 64
+        (dict(part=100, kernel=1), 2),          # generic partition not a multiple of 64
         (dict(kernel=9), 4),
         (dict(desc=dict(nb=2**28)), 2),         # num_blocks * block_size >= 2^31
     ],

@@ -1,0 +1,165 @@
+"""Host model of the fast decode kernel's work split (its integer arithmetic, step by step).
+
+The kernel gives wave w the tiles [w*Nt/W, (w+1)*Nt/W) of all (sequence, KV head,
+16-token tile) triples, finds its first sequence with a two-level prefix sum
+(8 sequences per lane, 64 lanes, ballot), walks the tiles with a cursor, keeps
+partial results at slot unit + w, and the wave that sees a unit's first tile
+records (first slot, count) with count = wave_of(last tile) - w + 1.  This model
+replays exactly that arithmetic and checks, for many length mixes and wave
+counts, that every tile is visited once, every index stays in range, slots never
+collide, and the recorded counts equal the number of waves that touch the unit.
+"""
+
+import numpy as np
+import pytest
+
+TOK = 16
+MAX_WAVES = 8192
+
+
+def tiles_of(ctx, table_tokens):
+    return 0 if (ctx < 0 or ctx > table_tokens) else (ctx + TOK - 1) // TOK
+
+
+def locate(ctx, table_tokens, hkv, c0):
+    """The kernel's second pass: lane l holds sequences base + 8l .. base + 8l + 7."""
+    S = len(ctx)
+    acc = 0
+    for base in range(0, S, 64 * 8):
+        nv = [[tiles_of(ctx[base + l * 8 + k], table_tokens) if base + l * 8 + k < S else 0
+               for k in range(8)] for l in range(64)]
+        s = [sum(x) for x in nv]
+        incl = list(np.cumsum(s))
+        chunk = int(incl[63]) * hkv
+        if c0 < acc + chunk:
+            mask = [acc + int(incl[l]) * hkv > c0 for l in range(64)]
+            L = mask.index(True)
+            b0 = acc + (int(incl[L]) - s[L]) * hkv
+            for k in range(8):
+                n = nv[L][k]
+                if c0 < b0 + n * hkv:
+                    return base + L * 8 + k, b0
+                b0 += n * hkv
+            raise AssertionError("lane L does not hold c0")
+        acc += chunk
+    return -1, 0
+
+
+def run_schedule(ctx, hkv, block_size, max_blocks, nwaves):
+    table_tokens = max_blocks * block_size
+    S = len(ctx)
+    n = [tiles_of(c, table_tokens) for c in ctx]
+    Nt = sum(n) * hkv
+    units = S * hkv
+    visits = {}
+    slots = {}
+    records = {}
+    if Nt == 0:
+        return Nt, visits, slots, records
+    W = min(Nt, nwaves)
+    seen_w = set()
+    for bid in range(nwaves):
+        w = (bid % 8) * (nwaves // 8) + bid // 8 if nwaves % 8 == 0 else bid
+        assert w not in seen_w
+        seen_w.add(w)
+        if w >= W:
+            continue
+        c0, c1 = w * Nt // W, (w + 1) * Nt // W
+        assert c1 > c0, "every wave below W owns at least one tile"
+        i, base = locate(ctx, table_tokens, hkv, c0)
+        assert 0 <= i < S
+        cur = dict(i=i, ctx=ctx[i], n=n[i], seq_base=base)
+        off = c0 - base
+        cur["g"], cur["b"] = off // cur["n"], off % cur["n"]
+        from_start = False
+        for t in range(c0, c1):
+            first = t == c0 or cur["b"] == 0
+            if first:
+                from_start = cur["b"] == 0
+            i, g, b = cur["i"], cur["g"], cur["b"]
+            assert 0 <= i < S and 0 <= g < hkv and 0 <= b < cur["n"]
+            tok0 = b * TOK
+            blk = tok0 // block_size
+            assert blk < max_blocks and tok0 % block_size + TOK <= block_size
+            valid = min(TOK, cur["ctx"] - tok0)
+            assert 1 <= valid <= TOK
+            assert cur["seq_base"] + g * cur["n"] + b == t, "cursor and tile index agree"
+            visits[t] = visits.get(t, 0) + 1
+            unit_end = b == cur["n"] - 1
+            if unit_end or t + 1 == c1:
+                u = i * hkv + g
+                complete = from_start and unit_end
+                if not complete:
+                    slot = u + w
+                    assert slot < units + MAX_WAVES
+                    assert slot not in slots, "partial slots collide"
+                    slots[slot] = (u, w)
+                if from_start:
+                    last_tile = cur["seq_base"] + g * cur["n"] + cur["n"] - 1
+                    w_last = ((last_tile + 1) * W - 1) // Nt
+                    records[u] = (u + w, w_last - w + 1)
+                    assert (records[u][1] == 1) == complete
+            # advance
+            if t + 1 < c1:
+                cur["b"] += 1
+                if cur["b"] == cur["n"]:
+                    cur["b"] = 0
+                    cur["g"] += 1
+                    if cur["g"] == hkv:
+                        cur["g"] = 0
+                        cur["seq_base"] += hkv * cur["n"]
+                        while True:
+                            cur["i"] += 1
+                            assert cur["i"] < S
+                            cur["ctx"] = ctx[cur["i"]]
+                            cur["n"] = tiles_of(cur["ctx"], table_tokens)
+                            if cur["n"]:
+                                break
+    return Nt, visits, slots, records
+
+
+def _cases():
+    rng = np.random.default_rng(0)
+    cases = [
+        ([17, 33, 35, 64], 1, 16, 4, 2048),
+        ([0, 0, 5, 0], 8, 16, 4, 64),
+        ([32768] * 8, 8, 16, 2048, 2048),
+        ([1] * 300, 8, 16, 1, 1000),
+        ([0, 1, 15, 16, 17, 100, 2000, 7, 4100, 33], 4, 16, 257, 3),
+        ([31, 32, 33, 64, 999], 1, 32, 32, 8192),
+        ([70, -3, 10**9, 5], 2, 64, 2, 24),  # bad lengths count as empty
+    ]
+    lens = np.clip(np.rint(np.exp(rng.normal(np.log(1024), 1.0, 256))), 1, 8192).astype(int).tolist()
+    cases.append((lens, 8, 16, 512, 2048))
+    cases.append((lens, 8, 16, 512, 2056))
+    cases.append((rng.integers(0, 3000, 700).tolist(), 2, 32, 94, 1536))  # S > 512: two chunks
+    for k in range(10):
+        S = int(rng.integers(1, 40))
+        B = int(rng.choice([16, 32, 64]))
+        maxb = int(rng.integers(1, 20))
+        lens = rng.integers(0, maxb * B + 1, S).tolist()
+        cases.append((lens, int(rng.choice([1, 2, 8])), B, maxb, int(rng.integers(1, 300))))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(len(_cases())))
+def test_schedule_covers_every_tile_once(case):
+    ctx, hkv, B, maxb, nwaves = _cases()[case]
+    Nt, visits, slots, records = run_schedule(ctx, hkv, B, maxb, nwaves)
+    assert len(visits) == Nt and all(v == 1 for v in visits.values())
+    table_tokens = maxb * B
+    touched = {}
+    for slot, (u, w) in slots.items():
+        touched.setdefault(u, []).append(w)
+    for i, c in enumerate(ctx):
+        for g in range(hkv):
+            u = i * hkv + g
+            if tiles_of(c, table_tokens) == 0:
+                assert u not in records
+                continue
+            first, count = records[u]
+            if count == 1:
+                assert u not in touched
+            else:
+                ws = sorted(touched[u])
+                assert ws == list(range(ws[0], ws[0] + count)) and first == u + ws[0]

@@ -36,10 +36,10 @@ def _kernels_for(w):
     return ks
 
 
-def _check_step(w, oracle_impl, what, partition_tokens=0, kernel=0):
+def _check_step(w, oracle_impl, what, partition_tokens=0, kernel=0, grid_waves=0):
     say(f"[gpu] {what}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"B={w.block_size} {w.dtype} T={partition_tokens} kernel={kernel}")
-    d, out = run_step(w, partition_tokens=partition_tokens, kernel=kernel)
+        f"B={w.block_size} {w.dtype} T={partition_tokens} kernel={kernel} waves={grid_waves}")
+    d, out = run_step(w, partition_tokens=partition_tokens, kernel=kernel, grid_waves=grid_waves)
     ref = oracle.decode_step(w, oracle=oracle_impl)
     assert np.array_equal(bits(d["k_cache"]), ref.k_cache_bits), f"{what}: K pool differs after write"
     assert np.array_equal(bits(d["v_cache"]), ref.v_cache_bits), f"{what}: V pool differs after write"
@@ -52,8 +52,24 @@ def _check_step(w, oracle_impl, what, partition_tokens=0, kernel=0):
 def test_config_step(name, oracle_impl):
     """Every workload at full size: write bit-exact, decode within tolerance, each kernel family."""
     w = make_config(name)
-    for k in _kernels_for(w):
+    ks = _kernels_for(w)
+    if w.dtype == torch.bfloat16:  # the fast path must be the one chosen for the bf16 workloads
+        assert pkv.PKV_KERNEL_FAST in ks
+        plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq,
+                                   pkv.CacheDesc(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, 1))
+        assert plan["kernel"] == "fast"
+    for k in ks:
         _check_step(w, oracle_impl, f"{name}/kernel{k}", kernel=k)
+
+
+@pytest.mark.parametrize("waves", [1, 3, 8, 64, 1000, 8192])
+def test_fast_wave_count_sweep(waves, oracle_impl):
+    """The fast kernel's split points move with the wave count; results stay within tolerance."""
+    w = make_custom([0, 1, 15, 16, 17, 100, 2000, 7, 4100, 33], 16, 4, 128, 16, torch.bfloat16, seed=9,
+                    pool_fill=0.8)
+    _check_step(w, oracle_impl, f"waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
+    w32 = make_custom([31, 32, 33, 64, 999], 8, 1, 128, 32, torch.bfloat16, seed=10, pool_fill=0.8)
+    _check_step(w32, oracle_impl, f"waves{waves}/B32", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
 
 
 SHAPES = [  # (lengths, Hq, Hkv, D, B, dtype)
