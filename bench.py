@@ -51,6 +51,9 @@ def parse_args(argv=None):
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per launch measured by rocprofv3 counters (optional)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="after the timed steps, copy a buffer of this many MiB three times "
+                        "(a plain copy of known size for scaling hardware byte counters)")
     return p.parse_args(argv)
 
 
@@ -116,7 +119,7 @@ def main(argv=None) -> int:
     plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
                                partition_tokens=args.partition_tokens, kernel=args.kernel)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty((max(plan["workspace_bytes"], 16) + 15) // 16 * 16, dtype=torch.uint8, device=dev)
 
     def write():
         pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
@@ -204,6 +207,18 @@ def main(argv=None) -> int:
         "torch": torch.__version__,
         "hip": torch.version.hip,
     }
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n
+        del src, dst
 
     if not args.no_parity:
         import oracle

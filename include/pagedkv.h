@@ -164,12 +164,13 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   opts          (host) NULL or settings
  *
  * Work splitting.  The generic kernel cuts every sequence into partitions of
- * plan.partition_tokens tokens.  The fast kernel lays all (sequence, KV head,
- * 16-token tile) triples end to end and gives each wave of its grid an equal
- * contiguous run of tiles, so a long sequence spreads over several waves and
- * many short ones share a wave.  Either way every piece yields a running max,
- * a softmax denominator and an unnormalised output, merged by a log-sum-exp
- * combine.  Results do not depend on the physical placement of blocks (the
+ * plan.partition_tokens tokens and merges them in a second kernel.  The fast
+ * kernel lays all (sequence, KV head, 16-token tile) triples end to end and
+ * gives each wave of its grid an equal contiguous run of tiles, so a long
+ * sequence spreads over several waves and many short ones share a wave; a
+ * second kernel merges the pieces of each (sequence, KV head).
+ * Either way every piece yields a running max, a softmax denominator and an
+ * unnormalised output, merged by a log-sum-exp combine.  Results do not depend on the physical placement of blocks (the
  * summation order is fixed by logical token positions and the wave count).
  * Calls that share a workspace must be serialised on one stream.
  */

@@ -137,6 +137,8 @@ def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_s
     return int(out.value)
 
 
+# One cached workspace per (device, stream): calls on one stream are ordered, so
+# they can share it.
 _workspaces: Dict[Tuple[torch.device, int], torch.Tensor] = {}
 
 
@@ -146,7 +148,7 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Optiona
     key = (device, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -177,7 +179,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     maxb = block_tables.shape[1]
     opts = _opts(partition_tokens, kernel, grid_waves)
     s = _stream(dev, stream)
-    need = paged_attn_workspace_bytes(S, Hq, maxb, desc, partition_tokens, kernel, grid_waves)
+    plan = paged_attn_plan(S, Hq, maxb, desc, partition_tokens, kernel, grid_waves)
+    need = plan["workspace_bytes"]
     if workspace is None:
         workspace = _workspace(dev, int(s.value or 0), need)
     elif need:

@@ -32,7 +32,7 @@ pkv_status check_desc(const pkv_cache_desc* c) {
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-    uint64_t rec_bytes;  // fast: int2 [S][Hkv]
+    uint64_t rec_bytes;  // fast: int2 (first partial slot, partial count) [S][Hkv]
     uint64_t ml_bytes;   // generic: float2 [S][Hq][P]; fast: float2 [slots][G]
     uint64_t acc_bytes;  // generic: float [S][Hq][P][D]; fast: float [slots][G][D]
     uint64_t total;
@@ -50,8 +50,9 @@ WorkspaceLayout generic_layout(int32_t num_seqs, int32_t num_q_heads, int32_t ma
     return w;
 }
 
-// Fast kernel: partial slot u + w for unit u = seq * Hkv + kv_head met by wave w;
-// at most (units + waves) slots, each holding the unit's G query heads.
+// Fast kernel: per-unit records first, then partial slot u + w for unit
+// u = seq * Hkv + kv_head met by wave w; at most (units + waves) slots, each
+// holding the unit's G query heads.
 WorkspaceLayout fast_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim) {
     WorkspaceLayout w{0, 0, 0, 0};
     const uint64_t units = (uint64_t)num_seqs * (uint64_t)num_kv_heads;
@@ -204,7 +205,7 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (plan.kernel == PKV_KERNEL_FAST) {
-        e = pkv::launch_decode_fast(a, s);  // partition kernel + merge
+        e = pkv::launch_decode_fast(a, s);  // tile kernel + merge kernel
     } else {
         e = pkv::launch_decode_generic(a, s);
         if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);

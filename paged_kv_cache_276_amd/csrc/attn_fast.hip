@@ -17,22 +17,25 @@
 //     dims per MFMA, so one load instruction reads 64 contiguous bytes of each
 //     of the 16 rows.  Lane t < 16 (t < 32 for G = 8) ends up with the scores
 //     of token t for four query heads.
-//   * online softmax in log2 units: the tile max per head is a 16-lane DPP
-//     reduction; the running max only moves when the tile max exceeds it by
-//     more than 8 (so exp2 stays <= 256 and the rescale of the accumulator is
-//     rare); p = exp2(s - m) with tail tokens masked by select.
+//   * online softmax in log2 units: the running max only moves when a score
+//     exceeds it by more than 8 (so exp2 stays <= 256); a ballot detects that
+//     case, and only then is the tile max reduced along the 16-lane row (DPP)
+//     and the accumulator rescaled; p = exp2(s - m), tail tokens masked by
+//     select.
 //   * P.V on the vector ALUs in fp32: lane l owns dims 8*(l%16) .. +7 of tokens
 //     4*i + l/16 (i = 0..3), i.e. each V load instruction reads 1 KiB
 //     contiguous; the weights p travel through 512 bytes of LDS.
 // When the wave leaves a (sequence, KV head) it folds the four lane groups,
-// then either normalises and writes the output row (it saw every tile of the
-// unit) or stores (m, l, acc) as a partial result; the wave that saw the
-// unit's first tile also records where the unit's partials start and how many
-// there are.  combine_fast_kernel merges the partials with log-sum-exp.
+// then either normalises and writes the output rows (it saw every tile of the
+// unit) or stores (m, l, acc) as a partial result at slot unit + wave; the
+// wave that saw the unit's first tile records the unit's first slot and
+// partial count.  merge_fast_kernel then merges the partials with log-sum-exp
+// in slot order and writes the rows of sequences without tiles.
 //
 // Block-table entries are fetched 64 at a time into a lane-indexed window and
-// picked out with readlane; the next tile's K, V and (on a unit change) q are
-// requested before the current tile is computed.
+// picked out with readlane.  Tile buffers form a ring: the loads of tiles
+// t + 1 and t + 2 (t + 1 only, for G = 8) are in flight while tile t is
+// computed.
 #include <math.h>
 
 #include <map>
@@ -95,6 +98,16 @@ __device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Wait for every outstanding vector-memory load (vmcnt 0; expcnt and lgkmcnt
+// left at their maxima).  Placed at the end of the rare branches that load
+// (block-table refill, a unit's q) so the common path's waits count only the
+// tile loads and the next tile stays in flight.
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 2^x with the hardware instruction alone (no denormal-range fix-up: softmax
+// weights below 2^-126 flush to zero, far below the fp32 accumulation error).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct Cursor {
     int i;             // sequence
     int g;             // KV head
@@ -102,6 +115,14 @@ struct Cursor {
     int n;             // tiles of the unit
     int ctx;           // tokens of the sequence
     int64_t seq_base;  // global index of the sequence's first tile
+};
+
+struct TileLoad {
+    uint4 k[4];  // MFMA B fragments of the 16 key rows
+    uint4 v[4];  // value rows 4*i + lane/16, dims 8*(lane%16) .. +7
+    Cursor c;    // which tile
+    int valid;   // tokens of the tile inside the sequence
+    bool bad;    // the block-table entry was outside the pool
 };
 
 }  // namespace
@@ -180,7 +201,6 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
             acc += chunk;
         }
     }
-
     if (i0 < 0) return;  // unreachable when the two passes agree; keeps every index below in range
 
     const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
@@ -205,20 +225,9 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
     const int r16 = lane & 15;  // MFMA column (token) / V column group
     const int grp = lane >> 4;  // MFMA k-group / V token phase
 
-    auto load_q = [&](const Cursor& c, uint4 (&qf)[4]) {
-        if (r16 < G) {
-            const uint4* src = reinterpret_cast<const uint4*>(
-                qbase + ((int64_t)c.i * Hq + (int64_t)c.g * G + r16) * kHd + grp * 8);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qf[kk] = src[kk * 4];
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qf[kk] = make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    // Issue the loads of tile c; returns its valid rows and whether its block id was bad.
-    auto fetch = [&](const Cursor& c, uint4 (&kf)[4], uint4 (&vf)[4], int& valid, bool& badt) {
+    // Issue the K and V loads of the tile under cursor c.
+    auto issue = [&](const Cursor& c, TileLoad& T) {
+        T.c = c;
         const int tok0 = c.b * kTok;
         const int blk = tok0 / BS;
         if (c.i != win_i || blk < win_b0 || blk >= win_b0 + kWave) {
@@ -226,19 +235,27 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
             win_b0 = blk;
             const int e = blk + lane;
             win = e < maxB ? bt[(int64_t)c.i * maxB + e] : -1;
+            drain_vmem();
         }
         int phys = read_lane(win, blk - win_b0);
-        badt = (unsigned)phys >= (unsigned)a.num_blocks;
-        if (badt) phys = 0;
-        valid = min(kTok, c.ctx - tok0);
+        T.bad = (unsigned)phys >= (unsigned)a.num_blocks;
+        if (T.bad) phys = 0;
+        T.valid = min(kTok, c.ctx - tok0);
+        // The tile's base address is wave-uniform: keep it in scalar registers
+        // and give the loads 32-bit lane offsets.
         const int64_t tile = (((int64_t)phys * Hkv + c.g) * BS + (tok0 % BS)) * kHd;
-        const uint4* kp = reinterpret_cast<const uint4*>(kbase + tile + r16 * kHd) + grp;
+        const uint32_t tlo = __builtin_amdgcn_readfirstlane((uint32_t)tile);
+        const uint32_t thi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tile >> 32));
+        const int64_t tile_s = (int64_t)(((uint64_t)thi << 32) | tlo);
+        const uint16_t* kt = kbase + tile_s;
+        const uint16_t* vt = vbase + tile_s;
+        const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kf[kk] = kp[kk * 4];
+        for (int kk = 0; kk < 4; ++kk) T.k[kk] = *reinterpret_cast<const uint4*>(kt + koff + kk * 32);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int row = min(4 * ii + grp, valid - 1);
-            vf[ii] = reinterpret_cast<const uint4*>(vbase + tile + row * kHd)[r16];
+            const uint32_t voff = (uint32_t)min(4 * ii + grp, T.valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
+            T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
         }
     };
 
@@ -253,42 +270,82 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
                     c.ctx = ctxp[c.i];
                     c.n = tiles_of(c.ctx, table_tokens);
                 } while (c.n == 0);
+                drain_vmem();
             }
         }
     };
 
     __shared__ float4 p_lds[16 * ROWS];
 
-    uint4 qc[4], qn[4], kc[4], vc[4], kn[4], vn[4];
-    int valid_n;
-    bool bad_n;
-    load_q(P, qn);
-    fetch(P, kn, vn, valid_n, bad_n);
-
+    uint4 qc[4];
     float acc[G][8];
     float m[4], l[4];
     bool bad = false, from_start = false;
 
-    for (int64_t t = c0; t < c1; ++t) {
-        const Cursor C = P;
-        const int valid = valid_n;
-        const bool bad_t = bad_n;
+    // Leave the current unit: write its output (the wave saw every tile of it)
+    // or a partial result at slot unit + wave; the wave that saw the unit's
+    // first tile records where the unit's partials start and how many there
+    // are (waves from the one holding its first tile to the one holding its
+    // last), for the merge kernel.
+    auto finish_unit = [&](const Cursor& C, bool unit_end) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            kc[k] = kn[k];
-            vc[k] = vn[k];
-        }
-        const bool first = (t == c0) || (C.b == 0);
-        if (first) {
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) qc[k] = qn[k];
+            for (int e = 0; e < 8; ++e) {
+                acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
+                acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
+            }
+        float lsum[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
+        const int64_t u = (int64_t)C.i * Hkv + C.g;
+        if (from_start && unit_end) {
+            if (lane < 16) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float inv = bad ? NAN : 1.f / read_lane(lsum[h & 3], 16 * (h >> 2));
+                    float4* o = reinterpret_cast<float4*>(
+                        a.out + ((int64_t)C.i * Hq + (int64_t)C.g * G + h) * kHd + 8 * lane);
+                    o[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
+                    o[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
+                }
+            }
+            if (lane == 0) a.ws_rec[u] = make_int2((int)(u + w), 1);
+            return;
         }
-        if (t + 1 < c1) {  // request the next tile before computing this one
-            advance(P);
-            if (P.b == 0) load_q(P, qn);
-            fetch(P, kn, vn, valid_n, bad_n);
+        const int64_t slot = u + w;
+        if (lane < 16) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float4* pa = reinterpret_cast<float4*>(a.ws_acc + (slot * G + h) * kHd + 8 * lane);
+                pa[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                pa[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+            }
         }
-        if (first) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
+            const float mh = read_lane(m[h & 3], 16 * (h >> 2));
+            if (lane == h) a.ws_ml[slot * G + h] = make_float2(mh, bad ? NAN : lh);
+        }
+        if (from_start && lane == 0) {
+            const int64_t last_tile = C.seq_base + (int64_t)C.g * C.n + C.n - 1;
+            const int64_t w_last = ((last_tile + 1) * W - 1) / Nt;
+            a.ws_rec[u] = make_int2((int)slot, (int)(w_last - w + 1));
+        }
+    };
+
+    // Entering a tile: at a unit's first tile (or the chunk's first) load the
+    // unit's q and reset the running state.  Called before the next tile's
+    // loads are issued, so its drain waits only for data this tile needs.
+    auto begin = [&](int64_t t, const TileLoad& T) {
+        const Cursor& C = T.c;
+        if (t == c0 || C.b == 0) {
+            const uint4* src = reinterpret_cast<const uint4*>(
+                qbase + ((int64_t)C.i * Hq + (int64_t)C.g * G + (r16 < G ? r16 : 0)) * kHd + grp * 8);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qc[kk] = r16 < G ? src[kk * 4] : make_uint4(0, 0, 0, 0);
+            drain_vmem();
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -301,30 +358,36 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
             bad = false;
             from_start = (C.b == 0);
         }
-        bad = bad || bad_t;
+    };
 
-        // scores of the 16 tokens for the (padded) query rows
+    // One tile: scores by MFMA, online softmax, P.V into the accumulator.
+    auto step = [&](int64_t t, const TileLoad& T) {
+        const Cursor& C = T.c;
+        bad = bad || T.bad;
+
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kk]), as_bf16x8(kc[kk]), sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kk]), as_bf16x8(T.k[kk]), sc, 0, 0, 0);
 
-        const bool tok_ok = r16 < valid;
-        float s[4], tm[4];
+        const bool tok_ok = r16 < T.valid;
+        float s[4];
+        bool need = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             s[r] = tok_ok ? sc[r] * qscale : -INFINITY;
-            tm[r] = row_max16(s[r]);
+            need = need || (s[r] > m[r] + kLazyRescale);
         }
-        bool need = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) need = need || (tm[r] > m[r] + kLazyRescale);
+        // The running max moves only when some score passes it by more than
+        // the threshold (always on a unit's first tile, rarely after); only
+        // then is the tile max reduced along the row and the state rescaled.
         if (__any(need && lane < 16 * ROWS)) {
             float alpha[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float mn = tm[r] > m[r] + kLazyRescale ? tm[r] : m[r];
-                alpha[r] = exp2f(m[r] - mn);
+                const float tm = row_max16(s[r]);
+                const float mn = tm > m[r] + kLazyRescale ? tm : m[r];
+                alpha[r] = fast_exp2(m[r] - mn);
                 m[r] = mn;
                 l[r] *= alpha[r];
             }
@@ -338,11 +401,16 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = exp2f(s[r] - m[r]);
+            p[r] = fast_exp2(s[r] - m[r]);
             l[r] += p[r];
         }
+        // The weights move from the score layout to the P.V layout through LDS.
+        // One wave per workgroup: LDS operations of a wave complete in order,
+        // the fences only keep the compiler from moving them.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         if (lane < 16 * ROWS) p_lds[lane] = make_float4(p[0], p[1], p[2], p[3]);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -354,7 +422,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
                 const float4 p1 = p_lds[16 + trow];
                 pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
             }
-            const uint4 u = vc[ii];
+            const uint4 u = T.v[ii];
             float vv[8];
             vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
             vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
@@ -365,96 +433,81 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], vv[e], acc[h][e]);
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 
         const bool unit_end = (C.b == C.n - 1);
-        if (unit_end || t + 1 == c1) {
-            // fold the four token phases: every lane group then holds the full sums
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
-                    acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
-                }
-            float lsum[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
-            const int u = C.i * Hkv + C.g;
-            const bool complete = from_start && unit_end;
-            if (complete) {
-                if (lane < 16) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
-                        const float inv = 1.f / lh;
-                        float* o = a.out + ((int64_t)C.i * Hq + (int64_t)C.g * G + h) * kHd + 8 * lane;
-                        float4 o0, o1;
-                        o0.x = acc[h][0] * inv; o0.y = acc[h][1] * inv; o0.z = acc[h][2] * inv; o0.w = acc[h][3] * inv;
-                        o1.x = acc[h][4] * inv; o1.y = acc[h][5] * inv; o1.z = acc[h][6] * inv; o1.w = acc[h][7] * inv;
-                        if (bad) o0 = o1 = make_float4(NAN, NAN, NAN, NAN);
-                        reinterpret_cast<float4*>(o)[0] = o0;
-                        reinterpret_cast<float4*>(o)[1] = o1;
-                    }
-                }
-            } else {
-                const int64_t slot = (int64_t)u + w;
-                if (lane < 16) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        float* pa = a.ws_acc + (slot * G + h) * kHd + 8 * lane;
-                        reinterpret_cast<float4*>(pa)[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-                        reinterpret_cast<float4*>(pa)[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-                    }
-                }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
-                    const float mh = read_lane(m[h & 3], 16 * (h >> 2));
-                    if (lane == 0) a.ws_ml[slot * G + h] = make_float2(mh, bad ? NAN : lh);
-                }
-            }
-            if (from_start && lane == 0) {
-                const int64_t last_tile = C.seq_base + (int64_t)C.g * C.n + C.n - 1;
-                const int64_t w_last = ((last_tile + 1) * W - 1) / Nt;
-                a.ws_rec[u] = make_int2(u + w, (int)(w_last - w + 1));
-            }
+        if (unit_end || t + 1 == c1) finish_unit(C, unit_end);
+    };
+
+    // Tile buffers in a ring: while tile t is computed, the next tiles are in
+    // flight (two of them for G <= 4; for G = 8 the wider accumulator leaves
+    // room for one).  Every phase issues exactly one tile's loads (past the
+    // end of the run it requests the tile issued last again, which the cache
+    // holds), so all paths issue the same loads in the same order and each
+    // wait counts exactly the loads it needs.
+    if constexpr (G <= 4) {
+        auto phase = [&](int64_t tt, TileLoad& cur, TileLoad& ahead) {
+            if (tt < c1) begin(tt, cur);
+            if (tt + 2 < c1) advance(P);
+            issue(P, ahead);  // tile tt + 2
+            if (tt < c1) step(tt, cur);
+        };
+        TileLoad X0, X1, X2;
+        issue(P, X0);
+        if (c0 + 1 < c1) advance(P);
+        issue(P, X1);
+        for (int64_t t = c0; t < c1; t += 3) {
+            phase(t, X0, X2);
+            phase(t + 1, X1, X0);
+            phase(t + 2, X2, X1);
+        }
+    } else {
+        auto phase = [&](int64_t tt, TileLoad& cur, TileLoad& ahead) {
+            if (tt < c1) begin(tt, cur);
+            if (tt + 1 < c1) advance(P);
+            issue(P, ahead);  // tile tt + 1
+            if (tt < c1) step(tt, cur);
+        };
+        TileLoad X0, X1;
+        issue(P, X0);
+        for (int64_t t = c0; t < c1; t += 2) {
+            phase(t, X0, X1);
+            phase(t + 1, X1, X0);
         }
     }
 }
 
-// One wave per (sequence, query head) row: merge the partial results of the
-// row's unit; rows finished by the partition kernel (one partial) are left
-// alone.  Empty sequences get zeros, out-of-range lengths NaN.
+// Merge kernel: one workgroup per (sequence, KV head) unit, one wave per query
+// head of the group.  Units the partition kernel finished (one partial) are
+// left alone; otherwise head h gets M = max_p m_p, L = sum_p 2^(m_p - M) l_p
+// and out = sum_p 2^(m_p - M) acc_p / L over the unit's partials in slot
+// order.  Sequences without tiles get zero rows (empty) or NaN rows (length
+// outside the table).  Lanes own two output columns each.
 template <int G>
-__global__ __launch_bounds__(64) void combine_fast_kernel(const DecodeArgs a, int table_tokens) {
-    const int lane = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int i = (int)(row / a.num_q_heads);
-    const int h = (int)(row % a.num_q_heads);
-    const int g = h / G, hh = h % G;
+__global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, int table_tokens) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int h = threadIdx.x / kWave;
+    const int64_t u = blockIdx.x;
+    const int i = (int)(u / a.num_kv_heads);
+    const int g = (int)(u % a.num_kv_heads);
     const int ctx = a.context_lens[i];
-    float* out = a.out + row * kHd + 2 * lane;
-    if (ctx < 0 || ctx > table_tokens) {
-        out[0] = NAN;
-        out[1] = NAN;
+    float2* out = reinterpret_cast<float2*>(
+        a.out + ((int64_t)i * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
+    if (tiles_of(ctx, table_tokens) == 0) {
+        const float v = ctx == 0 ? 0.f : NAN;
+        *out = make_float2(v, v);
         return;
     }
-    if (ctx == 0) {
-        out[0] = 0.f;
-        out[1] = 0.f;
-        return;
-    }
-    const int2 rec = a.ws_rec[(int64_t)i * a.num_kv_heads + g];
+    const int2 rec = a.ws_rec[u];
     const int np = rec.y;
     if (np == 1) return;
     const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
     if (np < 1 || rec.x < 0 || (int64_t)rec.x + np > slots) {  // never written: refuse to read
-        out[0] = NAN;
-        out[1] = NAN;
+        *out = make_float2(NAN, NAN);
         return;
     }
-    const float2* ml = a.ws_ml + (int64_t)rec.x * G + hh;
+    const float2* ml = a.ws_ml + (int64_t)rec.x * G + h;
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[(int64_t)p * G].x);
     M = wave_max(M);
@@ -464,16 +517,31 @@ __global__ __launch_bounds__(64) void combine_fast_kernel(const DecodeArgs a, in
         L += exp2f(v.x - M) * v.y;
     }
     L = wave_sum(L);
+    const float* acc = a.ws_acc + ((int64_t)rec.x * G + h) * kHd + 2 * lane;
+    const int64_t pstride = (int64_t)G * kHd;
     float o0 = 0.f, o1 = 0.f;
-    const float* acc = a.ws_acc + ((int64_t)rec.x * G + hh) * kHd + 2 * lane;
-    for (int p = 0; p < np; ++p) {
+    int p = 0;
+    for (; p + 4 <= np; p += 4) {  // four partials' loads in flight at once
+        float2 v[4], mlv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = *reinterpret_cast<const float2*>(acc + (p + k) * pstride);
+            mlv[k] = ml[(int64_t)(p + k) * G];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float wgt = exp2f(mlv[k].x - M);
+            o0 = fmaf(wgt, v[k].x, o0);
+            o1 = fmaf(wgt, v[k].y, o1);
+        }
+    }
+    for (; p < np; ++p) {
+        const float2 v = *reinterpret_cast<const float2*>(acc + p * pstride);
         const float wgt = exp2f(ml[(int64_t)p * G].x - M);
-        const float2 v = *reinterpret_cast<const float2*>(acc + (int64_t)p * G * kHd);
         o0 = fmaf(wgt, v.x, o0);
         o1 = fmaf(wgt, v.y, o1);
     }
-    out[0] = o0 / L;
-    out[1] = o1 / L;
+    *out = make_float2(o0 / L, o1 / L);
 }
 
 namespace {
@@ -507,7 +575,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_fast_kernel<BS, G>), dim3(waves), dim3(kWave), 0, stream, a, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_combine_fast(a, stream);
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+    hipLaunchKernelGGL((merge_fast_kernel<G>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
+                       a.max_blocks_per_seq * BS);
+    return hipGetLastError();
 }
 
 template <int BS>
@@ -536,20 +607,6 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
         case 64: return by_group<64>(a, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_combine_fast(const DecodeArgs& a, hipStream_t stream) {
-    const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
-    if (rows == 0) return hipSuccess;
-    const int table_tokens = a.max_blocks_per_seq * a.block_size;
-    switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: hipLaunchKernelGGL(combine_fast_kernel<1>, dim3((unsigned)rows), dim3(kWave), 0, stream, a, table_tokens); break;
-        case 2: hipLaunchKernelGGL(combine_fast_kernel<2>, dim3((unsigned)rows), dim3(kWave), 0, stream, a, table_tokens); break;
-        case 4: hipLaunchKernelGGL(combine_fast_kernel<4>, dim3((unsigned)rows), dim3(kWave), 0, stream, a, table_tokens); break;
-        case 8: hipLaunchKernelGGL(combine_fast_kernel<8>, dim3((unsigned)rows), dim3(kWave), 0, stream, a, table_tokens); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -44,7 +44,6 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_combine_fast(const DecodeArgs& a, hipStream_t stream);
 
 bool generic_supports(int32_t dtype, int32_t head_dim, int32_t group);
 bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

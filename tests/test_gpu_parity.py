@@ -234,6 +234,23 @@ def test_write_bit_patterns():
         assert torch.equal(dv.cpu().view(itype), ev.view(itype))
 
 
+def test_fast_caller_workspace_reuse(oracle_impl):
+    """A caller-owned workspace full of garbage, reused across calls with different wave counts."""
+    w = make_custom([100, 3000, 17, 640, 0], 16, 4, 128, 16, torch.bfloat16, seed=81)
+    d = to_device(w)
+    plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"])
+    assert plan["kernel"] == "fast"
+    ws = torch.full(((plan["workspace_bytes"] + 15) // 16 * 16,), 0x5A, dtype=torch.uint8, device=d["q"].device)
+    pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    ref = oracle.decode_step(w, oracle=oracle_impl)
+    for waves in (0, 5, 64, 1, 0):
+        out = torch.full((w.num_seqs, w.num_q_heads, w.head_dim), float("nan"), device=d["q"].device)
+        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                              w.scale, out=out, workspace=ws, grid_waves=waves)
+        torch.cuda.synchronize()
+        assert_parity(out, ref.out, f"workspace reuse waves={waves}")
+
+
 def test_workspace_errors_raise():
     w = make_custom([3000], 8, 2, 128, 16, torch.bfloat16, seed=71)
     d = to_device(w)
