@@ -47,6 +47,7 @@ def parse_args(argv=None):
                    choices=["tiny", "llama8b_b64", "hc_b256", "long32k", "shared_prefix"])
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 fast")
+    p.add_argument("--grid-waves", type=int, default=0, help="fast kernel: waves sharing the work (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -117,7 +118,8 @@ def main(argv=None) -> int:
         "slot_mapping": torch.from_numpy(w.slot_mapping).to(dev),
     }
     plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
-                               partition_tokens=args.partition_tokens, kernel=args.kernel)
+                               partition_tokens=args.partition_tokens, kernel=args.kernel,
+                               grid_waves=args.grid_waves)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = torch.empty((max(plan["workspace_bytes"], 16) + 15) // 16 * 16, dtype=torch.uint8, device=dev)
 
@@ -127,7 +129,7 @@ def main(argv=None) -> int:
     def decode():
         pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                               w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
-                              kernel=args.kernel)
+                              kernel=args.kernel, grid_waves=args.grid_waves)
 
     print(f"[bench] warmup {args.warmup} steps, plan {plan}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -188,6 +190,7 @@ def main(argv=None) -> int:
             "lengths": w.meta.get("lengths", "fixed"),
             "kernel": plan["kernel"],
             "partition_tokens": plan["partition_tokens"],
+            "grid_waves": plan["grid_blocks"],
         },
         "roofline": {
             "bound": "hbm",

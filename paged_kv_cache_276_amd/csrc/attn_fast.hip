@@ -118,20 +118,26 @@ struct Cursor {
 };
 
 struct TileLoad {
-    uint4 k[4];  // MFMA B fragments of the 16 key rows
-    uint4 v[4];  // value rows 4*i + lane/16, dims 8*(lane%16) .. +7
-    Cursor c;    // which tile
-    int valid;   // tokens of the tile inside the sequence
-    bool bad;    // the block-table entry was outside the pool
+    uint4 k[4];      // MFMA B fragments of the 16 key rows
+    uint4 v[4];      // value rows 4*i + lane/16, dims 8*(lane%16) .. +7
+    uint32_t flags;  // valid rows | run << 8 | kFirst | kLast | kBad (the tile's record)
 };
+
+constexpr int kSegTiles = 128;  // tiles per segment (two per lane in the set-up)
+constexpr uint32_t kFirst = 1u << 16;  // tile 0 of its unit
+constexpr uint32_t kLast = 1u << 17;   // last tile of its unit
+constexpr uint32_t kBad = 1u << 18;    // block-table entry outside the pool
 
 }  // namespace
 
 template <int BS, int G>
-__global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, float qscale) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(const DecodeArgs a,
+                                                                                                  float qscale) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
     static_assert(BS % kTok == 0, "block size");
-    constexpr int ROWS = (G + 3) / 4;  // 16-lane rows that hold scores
+    constexpr int ROWS = (G + 3) / 4;       // 16-lane rows that hold scores
+    constexpr int kQv = (G * kHd * 2 + 1023) / 1024;  // 16-byte loads per lane for a unit's q rows
+    constexpr int kSegRuns = G == 8 ? 4 : 8;          // runs (pieces of units) per segment
     const int lane = threadIdx.x;
     const int nwaves = gridDim.x;
     const int bid = blockIdx.x;
@@ -208,6 +214,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
     const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_cache);
     const int32_t* __restrict__ bt = a.block_tables;
 
+    // Cursor at the next tile still to be placed in a segment.
     Cursor P;
     P.i = i0;
     P.ctx = ctxp[i0];
@@ -219,75 +226,33 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
         P.b = (int)(off % P.n);
     }
 
-    // block-table window: lane k holds entry win_b0 + k of sequence win_i
-    int win = -1, win_i = -1, win_b0 = 0;
-
     const int r16 = lane & 15;  // MFMA column (token) / V column group
     const int grp = lane >> 4;  // MFMA k-group / V token phase
 
-    // Issue the K and V loads of the tile under cursor c.
-    auto issue = [&](const Cursor& c, TileLoad& T) {
-        T.c = c;
-        const int tok0 = c.b * kTok;
-        const int blk = tok0 / BS;
-        if (c.i != win_i || blk < win_b0 || blk >= win_b0 + kWave) {
-            win_i = c.i;
-            win_b0 = blk;
-            const int e = blk + lane;
-            win = e < maxB ? bt[(int64_t)c.i * maxB + e] : -1;
-            drain_vmem();
-        }
-        int phys = read_lane(win, blk - win_b0);
-        T.bad = (unsigned)phys >= (unsigned)a.num_blocks;
-        if (T.bad) phys = 0;
-        T.valid = min(kTok, c.ctx - tok0);
-        // The tile's base address is wave-uniform: keep it in scalar registers
-        // and give the loads 32-bit lane offsets.
-        const int64_t tile = (((int64_t)phys * Hkv + c.g) * BS + (tok0 % BS)) * kHd;
-        const uint32_t tlo = __builtin_amdgcn_readfirstlane((uint32_t)tile);
-        const uint32_t thi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tile >> 32));
-        const int64_t tile_s = (int64_t)(((uint64_t)thi << 32) | tlo);
-        const uint16_t* kt = kbase + tile_s;
-        const uint16_t* vt = vbase + tile_s;
-        const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) T.k[kk] = *reinterpret_cast<const uint4*>(kt + koff + kk * 32);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const uint32_t voff = (uint32_t)min(4 * ii + grp, T.valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
-            T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
-        }
-    };
-
-    auto advance = [&](Cursor& c) {
-        if (++c.b == c.n) {
-            c.b = 0;
-            if (++c.g == Hkv) {
-                c.g = 0;
-                c.seq_base += (int64_t)Hkv * c.n;
-                do {
-                    ++c.i;
-                    c.ctx = ctxp[c.i];
-                    c.n = tiles_of(c.ctx, table_tokens);
-                } while (c.n == 0);
-                drain_vmem();
-            }
-        }
-    };
-
+    // Per-segment tables in LDS (one wave per workgroup):
+    //   rec[k]   tile k: element offset of its 16 K/V rows in the pools (x, y),
+    //            valid rows | run << 8 | flags (z)
+    //   qrow[r]  the G query rows of run r's (sequence, KV head), as stored in q
+    //   run[r]   run r's sequence, KV head, tile count of the unit, first tile
+    //            within the unit; seq_base, first segment slot, sequence length
+    __shared__ uint4 rec_lds[kSegTiles];
+    __shared__ uint4 q_lds[kSegRuns][kQv * kWave];
+    __shared__ int4 run_lds[kSegRuns][2];
     __shared__ float4 p_lds[16 * ROWS];
 
     uint4 qc[4];
     float acc[G][8];
     float m[4], l[4];
     bool bad = false, from_start = false;
+    int ui = 0, ug = 0, un = 1;  // unit being accumulated
+    int64_t useq_base = 0;
 
     // Leave the current unit: write its output (the wave saw every tile of it)
     // or a partial result at slot unit + wave; the wave that saw the unit's
     // first tile records where the unit's partials start and how many there
     // are (waves from the one holding its first tile to the one holding its
     // last), for the merge kernel.
-    auto finish_unit = [&](const Cursor& C, bool unit_end) {
+    auto finish_unit = [&](bool unit_end) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -298,14 +263,14 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
         float lsum[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
-        const int64_t u = (int64_t)C.i * Hkv + C.g;
+        const int64_t u = (int64_t)ui * Hkv + ug;
         if (from_start && unit_end) {
             if (lane < 16) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float inv = bad ? NAN : 1.f / read_lane(lsum[h & 3], 16 * (h >> 2));
                     float4* o = reinterpret_cast<float4*>(
-                        a.out + ((int64_t)C.i * Hq + (int64_t)C.g * G + h) * kHd + 8 * lane);
+                        a.out + ((int64_t)ui * Hq + (int64_t)ug * G + h) * kHd + 8 * lane);
                     o[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
                     o[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
                 }
@@ -329,152 +294,270 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(const DecodeArgs a, flo
             if (lane == h) a.ws_ml[slot * G + h] = make_float2(mh, bad ? NAN : lh);
         }
         if (from_start && lane == 0) {
-            const int64_t last_tile = C.seq_base + (int64_t)C.g * C.n + C.n - 1;
+            const int64_t last_tile = useq_base + (int64_t)ug * un + un - 1;
             const int64_t w_last = ((last_tile + 1) * W - 1) / Nt;
             a.ws_rec[u] = make_int2((int)slot, (int)(w_last - w + 1));
         }
     };
 
-    // Entering a tile: at a unit's first tile (or the chunk's first) load the
-    // unit's q and reset the running state.  Called before the next tile's
-    // loads are issued, so its drain waits only for data this tile needs.
-    auto begin = [&](int64_t t, const TileLoad& T) {
-        const Cursor& C = T.c;
-        if (t == c0 || C.b == 0) {
-            const uint4* src = reinterpret_cast<const uint4*>(
-                qbase + ((int64_t)C.i * Hq + (int64_t)C.g * G + (r16 < G ? r16 : 0)) * kHd + grp * 8);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qc[kk] = r16 < G ? src[kk * 4] : make_uint4(0, 0, 0, 0);
-            drain_vmem();
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                m[r] = -INFINITY;
-                l[r] = 0.f;
+    for (int64_t seg0 = c0; seg0 < c1;) {
+        // ---- segment set-up: walk up to kSegRuns runs (pieces of units) and
+        // kSegTiles tiles, then request every block-table entry and q row of
+        // the segment at once and park them in LDS.
+        const int room = (int)min((int64_t)kSegTiles, c1 - seg0);
+        int nruns = 0, k = 0;
+        while (k < room && nruns < kSegRuns) {  // wave-uniform walk
+            const int len = min(P.n - P.b, room - k);
+            if (lane == 0) {
+                run_lds[nruns][0] = make_int4(P.i, P.g, P.n, P.b);
+                run_lds[nruns][1] = make_int4((int)(uint32_t)P.seq_base,
+                                              (int)(uint32_t)((uint64_t)P.seq_base >> 32), k, P.ctx);
             }
-            bad = false;
-            from_start = (C.b == 0);
-        }
-    };
-
-    // One tile: scores by MFMA, online softmax, P.V into the accumulator.
-    auto step = [&](int64_t t, const TileLoad& T) {
-        const Cursor& C = T.c;
-        bad = bad || T.bad;
-
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kk]), as_bf16x8(T.k[kk]), sc, 0, 0, 0);
-
-        const bool tok_ok = r16 < T.valid;
-        float s[4];
-        bool need = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[r] = tok_ok ? sc[r] * qscale : -INFINITY;
-            need = need || (s[r] > m[r] + kLazyRescale);
-        }
-        // The running max moves only when some score passes it by more than
-        // the threshold (always on a unit's first tile, rarely after); only
-        // then is the tile max reduced along the row and the state rescaled.
-        if (__any(need && lane < 16 * ROWS)) {
-            float alpha[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float tm = row_max16(s[r]);
-                const float mn = tm > m[r] + kLazyRescale ? tm : m[r];
-                alpha[r] = fast_exp2(m[r] - mn);
-                m[r] = mn;
-                l[r] *= alpha[r];
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float ah = read_lane(alpha[h & 3], 16 * (h >> 2));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+            k += len;
+            ++nruns;
+            P.b += len;
+            if (P.b == P.n && seg0 + k < c1) {  // next unit (more tiles follow)
+                P.b = 0;
+                if (++P.g == Hkv) {
+                    P.g = 0;
+                    P.seq_base += (int64_t)Hkv * P.n;
+                    do {
+                        ++P.i;
+                        P.ctx = ctxp[P.i];
+                        P.n = tiles_of(P.ctx, table_tokens);
+                    } while (P.n == 0);
+                }
             }
         }
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = fast_exp2(s[r] - m[r]);
-            l[r] += p[r];
-        }
-        // The weights move from the score layout to the P.V layout through LDS.
-        // One wave per workgroup: LDS operations of a wave complete in order,
-        // the fences only keep the compiler from moving them.
+        const int seg_len = k;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (lane < 16 * ROWS) p_lds[lane] = make_float4(p[0], p[1], p[2], p[3]);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
-
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // q rows: run r's G rows are G * 256 contiguous bytes of q; lane l moves
+        // bytes [16 l, 16 l + 16) of every 1 KiB piece.
+        uint4 qv[kSegRuns][kQv];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int trow = 4 * ii + grp;
-            float pw[8];
-            const float4 p0 = p_lds[trow];
-            pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
-            if (G == 8) {
-                const float4 p1 = p_lds[16 + trow];
-                pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
+        for (int r = 0; r < kSegRuns; ++r) {
+            if (r < nruns) {
+                const int4 d = run_lds[r][0];
+                const uint4* qsrc = reinterpret_cast<const uint4*>(
+                    qbase + ((int64_t)d.x * Hq + (int64_t)d.y * G) * kHd);
+#pragma unroll
+                for (int v = 0; v < kQv; ++v) {
+                    const int idx = v * kWave + lane;
+                    qv[r][v] = idx < G * kHd / 8 ? qsrc[idx] : make_uint4(0, 0, 0, 0);
+                }
             }
-            const uint4 u = T.v[ii];
-            float vv[8];
-            vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
-            vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
-            vv[4] = bf16_lo(u.z); vv[5] = bf16_hi(u.z);
-            vv[6] = bf16_lo(u.w); vv[7] = bf16_hi(u.w);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], vv[e], acc[h][e]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        // tile records: lane j covers tiles j and j + 64 of the segment
+        int phys[2], trun[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int j = lane + kWave * half;
+            int r = 0;
+            for (int q = 1; q < nruns; ++q)
+                if (j >= run_lds[q][1].z) r = q;
+            trun[half] = r;
+            const int4 d = run_lds[r][0];
+            const int b = d.w + (j - run_lds[r][1].z);
+            phys[half] = j < seg_len ? bt[(int64_t)d.x * maxB + (b * kTok) / BS] : 0;
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int j = lane + kWave * half;
+            if (j < seg_len) {
+                const int r = trun[half];
+                const int4 d = run_lds[r][0];
+                const int4 e = run_lds[r][1];
+                const int b = d.w + (j - e.z);
+                const int tok0 = b * kTok;
+                const bool badp = (unsigned)phys[half] >= (unsigned)a.num_blocks;
+                const int ph = badp ? 0 : phys[half];
+                const int64_t off = (((int64_t)ph * Hkv + d.y) * BS + (tok0 % BS)) * kHd;
+                const uint32_t flags = (uint32_t)min(kTok, e.w - tok0) | ((uint32_t)r << 8) |
+                                       (b == 0 ? kFirst : 0u) | (b == d.z - 1 ? kLast : 0u) | (badp ? kBad : 0u);
+                rec_lds[j] = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), flags, 0u);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kSegRuns; ++r)
+            if (r < nruns)
+#pragma unroll
+                for (int v = 0; v < kQv; ++v) q_lds[r][v * kWave + lane] = qv[r][v];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        const bool unit_end = (C.b == C.n - 1);
-        if (unit_end || t + 1 == c1) finish_unit(C, unit_end);
-    };
+        // ---- the segment's tiles
+        // Issue the K and V loads of segment tile kk.  The tile's base address
+        // is wave-uniform: it goes to scalar registers, the loads take 32-bit
+        // lane offsets.
+        auto issue = [&](int kk, TileLoad& T) {
+            const uint4 rv = rec_lds[kk];
+            const uint32_t tlo = __builtin_amdgcn_readfirstlane(rv.x);
+            const uint32_t thi = __builtin_amdgcn_readfirstlane(rv.y);
+            T.flags = __builtin_amdgcn_readfirstlane(rv.z);
+            const int64_t tile_s = (int64_t)(((uint64_t)thi << 32) | tlo);
+            const int valid = (int)(T.flags & 0xffu);
+            const uint16_t* kt = kbase + tile_s;
+            const uint16_t* vt = vbase + tile_s;
+            const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
+                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+            }
+        };
 
-    // Tile buffers in a ring: while tile t is computed, the next tiles are in
-    // flight (two of them for G <= 4; for G = 8 the wider accumulator leaves
-    // room for one).  Every phase issues exactly one tile's loads (past the
-    // end of the run it requests the tile issued last again, which the cache
-    // holds), so all paths issue the same loads in the same order and each
-    // wait counts exactly the loads it needs.
-    if constexpr (G <= 4) {
-        auto phase = [&](int64_t tt, TileLoad& cur, TileLoad& ahead) {
-            if (tt < c1) begin(tt, cur);
-            if (tt + 2 < c1) advance(P);
-            issue(P, ahead);  // tile tt + 2
-            if (tt < c1) step(tt, cur);
+        // Entering a tile: at a unit's first tile (or the chunk's first) take
+        // the unit's q from LDS and reset the running state.
+        auto begin = [&](int64_t t, const TileLoad& T) {
+            if (t == c0 || (T.flags & kFirst)) {
+                const int r = (int)((T.flags >> 8) & 0xffu);
+                const int4 r0 = run_lds[r][0];
+                const int4 r1 = run_lds[r][1];
+                ui = __builtin_amdgcn_readfirstlane(r0.x);
+                ug = __builtin_amdgcn_readfirstlane(r0.y);
+                un = __builtin_amdgcn_readfirstlane(r0.z);
+                useq_base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(r1.y) << 32) |
+                                      (uint32_t)__builtin_amdgcn_readfirstlane(r1.x));
+                const uint16_t* qrow = reinterpret_cast<const uint16_t*>(&q_lds[r][0]);
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(qrow + (r16 < G ? r16 : 0) * kHd + kq * 32 + grp * 8);
+                    qc[kq] = r16 < G ? v : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    m[r2] = -INFINITY;
+                    l[r2] = 0.f;
+                }
+                bad = false;
+                from_start = (T.flags & kFirst) != 0;
+            }
         };
-        TileLoad X0, X1, X2;
-        issue(P, X0);
-        if (c0 + 1 < c1) advance(P);
-        issue(P, X1);
-        for (int64_t t = c0; t < c1; t += 3) {
-            phase(t, X0, X2);
-            phase(t + 1, X1, X0);
-            phase(t + 2, X2, X1);
-        }
-    } else {
-        auto phase = [&](int64_t tt, TileLoad& cur, TileLoad& ahead) {
-            if (tt < c1) begin(tt, cur);
-            if (tt + 1 < c1) advance(P);
-            issue(P, ahead);  // tile tt + 1
-            if (tt < c1) step(tt, cur);
+
+        // One tile: scores by MFMA, online softmax, P.V into the accumulator.
+        auto step = [&](int64_t t, const TileLoad& T) {
+            bad = bad || (T.flags & kBad);
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kq]), as_bf16x8(T.k[kq]), sc, 0, 0, 0);
+
+            const bool tok_ok = r16 < (int)(T.flags & 0xffu);
+            float s[4];
+            bool need = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[r] = tok_ok ? sc[r] * qscale : -INFINITY;
+                need = need || (s[r] > m[r] + kLazyRescale);
+            }
+            // The running max moves only when some score passes it by more
+            // than the threshold (always on a unit's first tile, rarely
+            // after); only then is the tile max reduced along the row and the
+            // state rescaled.
+            if (__any(need && lane < 16 * ROWS)) {
+                float alpha[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float tm = row_max16(s[r]);
+                    const float mn = tm > m[r] + kLazyRescale ? tm : m[r];
+                    alpha[r] = fast_exp2(m[r] - mn);
+                    m[r] = mn;
+                    l[r] *= alpha[r];
+                }
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float ah = read_lane(alpha[h & 3], 16 * (h >> 2));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+                }
+            }
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = fast_exp2(s[r] - m[r]);
+                l[r] += p[r];
+            }
+            // The weights move from the score layout to the P.V layout through
+            // LDS.  One wave per workgroup: LDS operations of a wave complete
+            // in order, the fences only keep the compiler from moving them.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            if (lane < 16 * ROWS) p_lds[lane] = make_float4(p[0], p[1], p[2], p[3]);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int trow = 4 * ii + grp;
+                float pw[8];
+                const float4 p0 = p_lds[trow];
+                pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
+                if (G == 8) {
+                    const float4 p1 = p_lds[16 + trow];
+                    pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
+                }
+                const uint4 u = T.v[ii];
+                float vv[8];
+                vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
+                vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
+                vv[4] = bf16_lo(u.z); vv[5] = bf16_hi(u.z);
+                vv[6] = bf16_lo(u.w); vv[7] = bf16_hi(u.w);
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], vv[e], acc[h][e]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+
+            const bool unit_end = (T.flags & kLast) != 0;
+            if (unit_end || t + 1 == c1) finish_unit(unit_end);
         };
-        TileLoad X0, X1;
-        issue(P, X0);
-        for (int64_t t = c0; t < c1; t += 2) {
-            phase(t, X0, X1);
-            phase(t + 1, X1, X0);
+
+        // Tile buffers in a ring: while tile kk is computed, the next tiles
+        // are in flight (two of them for G <= 4; for G = 8 the wider
+        // accumulator leaves room for one).  Every phase issues exactly one
+        // tile's loads (past the end of the segment it requests its last tile
+        // again, which the cache holds), so all paths issue the same loads in
+        // the same order and each wait counts exactly the loads it needs.
+        if constexpr (G <= 4) {
+            auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
+                if (kk < seg_len) begin(seg0 + kk, cur);
+                issue(min(kk + 2, seg_len - 1), ahead);
+                if (kk < seg_len) step(seg0 + kk, cur);
+            };
+            TileLoad X0, X1, X2;
+            issue(0, X0);
+            issue(min(1, seg_len - 1), X1);
+            for (int kk = 0; kk < seg_len; kk += 3) {
+                phase(kk, X0, X2);
+                phase(kk + 1, X1, X0);
+                phase(kk + 2, X2, X1);
+            }
+        } else {
+            auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
+                if (kk < seg_len) begin(seg0 + kk, cur);
+                issue(min(kk + 1, seg_len - 1), ahead);
+                if (kk < seg_len) step(seg0 + kk, cur);
+            };
+            TileLoad X0, X1;
+            issue(0, X0);
+            for (int kk = 0; kk < seg_len; kk += 2) {
+                phase(kk, X0, X1);
+                phase(kk + 1, X1, X0);
+            }
         }
+        seg0 += seg_len;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 

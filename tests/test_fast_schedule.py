@@ -15,6 +15,7 @@ import pytest
 
 TOK = 16
 MAX_WAVES = 8192
+SEG_TILES = 128
 
 
 def tiles_of(ctx, table_tokens):
@@ -45,7 +46,49 @@ def locate(ctx, table_tokens, hkv, c0):
     return -1, 0
 
 
-def run_schedule(ctx, hkv, block_size, max_blocks, nwaves):
+def segment_walk(ctx, hkv, block_size, max_blocks, c0, c1, cur, seg_runs):
+    """The kernel's segment set-up: runs of <= seg_runs pieces and <= SEG_TILES tiles.
+
+    Yields, per segment, the (sequence, KV head, tile) of every tile with its
+    block-table index, as the per-tile records would hold them."""
+    table_tokens = max_blocks * block_size
+    P = dict(cur)
+    seg0 = c0
+    while seg0 < c1:
+        room = min(SEG_TILES, c1 - seg0)
+        runs, k = [], 0
+        while k < room and len(runs) < seg_runs:
+            ln = min(P["n"] - P["b"], room - k)
+            assert ln > 0
+            runs.append((P["i"], P["g"], P["n"], P["b"], k, P["ctx"]))
+            k += ln
+            P["b"] += ln
+            if P["b"] == P["n"] and seg0 + k < c1:
+                P["b"] = 0
+                P["g"] += 1
+                if P["g"] == hkv:
+                    P["g"] = 0
+                    while True:
+                        P["i"] += 1
+                        assert P["i"] < len(ctx)
+                        P["ctx"] = ctx[P["i"]]
+                        P["n"] = tiles_of(P["ctx"], table_tokens)
+                        if P["n"]:
+                            break
+        seg_len = k
+        tiles = []
+        for j in range(seg_len):
+            r = max(q for q in range(len(runs)) if j >= runs[q][4])
+            i, g, n, b0, k0, c = runs[r]
+            b = b0 + (j - k0)
+            assert 0 <= b < n and (b * TOK) // block_size < max_blocks
+            assert 1 <= min(TOK, c - b * TOK) <= TOK
+            tiles.append((i, g, b))
+        yield tiles
+        seg0 += seg_len
+
+
+def run_schedule(ctx, hkv, block_size, max_blocks, nwaves, seg_runs=8):
     table_tokens = max_blocks * block_size
     S = len(ctx)
     n = [tiles_of(c, table_tokens) for c in ctx]
@@ -71,8 +114,13 @@ def run_schedule(ctx, hkv, block_size, max_blocks, nwaves):
         cur = dict(i=i, ctx=ctx[i], n=n[i], seq_base=base)
         off = c0 - base
         cur["g"], cur["b"] = off // cur["n"], off % cur["n"]
+        start_cursor = dict(cur)
+        walked = [x for seg in segment_walk(ctx, hkv, block_size, max_blocks, c0, c1, start_cursor, seg_runs)
+                  for x in seg]
+        assert len(walked) == c1 - c0
         from_start = False
         for t in range(c0, c1):
+            assert walked[t - c0] == (cur["i"], cur["g"], cur["b"]), "segment walk and cursor disagree"
             first = t == c0 or cur["b"] == 0
             if first:
                 from_start = cur["b"] == 0
@@ -142,10 +190,11 @@ def _cases():
     return cases
 
 
+@pytest.mark.parametrize("seg_runs", [8, 4])
 @pytest.mark.parametrize("case", range(len(_cases())))
-def test_schedule_covers_every_tile_once(case):
+def test_schedule_covers_every_tile_once(case, seg_runs):
     ctx, hkv, B, maxb, nwaves = _cases()[case]
-    Nt, visits, slots, records = run_schedule(ctx, hkv, B, maxb, nwaves)
+    Nt, visits, slots, records = run_schedule(ctx, hkv, B, maxb, nwaves, seg_runs)
     assert len(visits) == Nt and all(v == 1 for v in visits.values())
     table_tokens = maxb * B
     touched = {}
