@@ -48,6 +48,10 @@ def parse_args(argv=None):
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 fast")
     p.add_argument("--grid-waves", type=int, default=0, help="fast kernel: waves sharing the work (0 = library choice)")
+    p.add_argument("--cold-steps", type=int, default=10,
+                   help="after the timed steps, time this many decode calls each preceded by "
+                        "reading --flush-mib of scratch (no KV bytes left in L2 or MALL)")
+    p.add_argument("--flush-mib", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -55,6 +59,10 @@ def parse_args(argv=None):
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="after the timed steps, copy a buffer of this many MiB three times "
                         "(a plain copy of known size for scaling hardware byte counters)")
+    p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: read two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                        "WRITE_SIZE; each directory also holds the run's JSON line as bench.json) "
+                        "and record the decode call's HBM bytes per launch in --traffic-json")
     return p.parse_args(argv)
 
 
@@ -97,8 +105,93 @@ def cpu_baseline(w) -> dict:
     }
 
 
+DECODE_KERNELS = ("decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel")
+
+
+def _counter_rows(run_dir: str):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {run_dir}, found {files}")
+    with open(files[0]) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _per_dispatch(rows, counter: str):
+    """(kernel name, value) per dispatch; a counter read per XCD or SE is summed."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        name, val = acc.get(key, (r["Kernel_Name"], 0.0))
+        acc[key] = (name, val + float(r["Counter_Value"]))
+    return [acc[k] for k in sorted(acc)]
+
+
+def ingest_counters(args) -> int:
+    """Turn FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per decode call.
+
+    Each counter is scaled by what it reads for the plain device-to-device copy
+    of known size that the profiled run made last (three copies of
+    ``copy_calibration_bytes``), so that the figure is in real HBM bytes."""
+    out = {}
+    meta = None
+    for counter, run_dir in (("FETCH_SIZE", args.ingest_counters[0]), ("WRITE_SIZE", args.ingest_counters[1])):
+        with open(os.path.join(run_dir, "bench.json")) as f:
+            line = [ln for ln in f if ln.startswith("{")][-1]
+        rec = json.loads(line)
+        disp = _per_dispatch(_counter_rows(run_dir), counter)
+        copies = [v for n, v in disp if "copyBuffer" in n][-3:]
+        nbytes = rec.get("copy_calibration_bytes")
+        if not nbytes or len(copies) != 3:
+            raise SystemExit(f"{run_dir}: the run made no calibration copies (--copy-calibration-mib)")
+        factor = nbytes / (statistics.mean(copies) * 1024.0)
+        per_kernel = {}
+        for name in DECODE_KERNELS:
+            vals = [v for n, v in disp if name in n]
+            if vals:
+                per_kernel[name] = statistics.mean(vals) * 1024.0 * factor
+        if not per_kernel:
+            raise SystemExit(f"{run_dir}: no decode kernel dispatches")
+        out[counter] = {"factor": factor, "per_kernel_bytes": per_kernel, "bytes": sum(per_kernel.values())}
+        cfg = rec["config"]
+        this = (cfg["workload"], cfg["kernel"], cfg["partition_tokens"], rec["algorithmic_bytes"]["total"])
+        if meta is not None and meta != this:
+            raise SystemExit("the two runs profiled different workloads")
+        meta = this
+    key = f"{meta[0]}/{meta[1]}/T{meta[2]}"
+    table = {}
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            table = json.load(f)
+    table[key] = {
+        "source_sha": _kernel_source_sha(),
+        "bytes_per_launch": out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"],
+        "read_bytes": out["FETCH_SIZE"]["bytes"],
+        "write_bytes": out["WRITE_SIZE"]["bytes"],
+        "read_per_kernel": out["FETCH_SIZE"]["per_kernel_bytes"],
+        "write_per_kernel": out["WRITE_SIZE"]["per_kernel_bytes"],
+        "fetch_factor": out["FETCH_SIZE"]["factor"],
+        "write_factor": out["WRITE_SIZE"]["factor"],
+        "algorithmic_bytes": meta[3],
+    }
+    os.makedirs(os.path.dirname(args.traffic_json), exist_ok=True)
+    with open(args.traffic_json, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({key: table[key]}))
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.ingest_counters:
+        return ingest_counters(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "the multi-GPU path is a design note, not a measured configuration"}))
@@ -193,6 +286,7 @@ def main(argv=None) -> int:
             "grid_waves": plan["grid_blocks"],
         },
         "roofline": {
+            "kernel": "paged_attn_decode (partition + merge kernels, one call)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
@@ -210,6 +304,24 @@ def main(argv=None) -> int:
         "torch": torch.__version__,
         "hip": torch.version.hip,
     }
+
+    if args.cold_steps > 0:
+        # The flush only reads: a written flush would leave dirty lines whose write-back
+        # lands inside the timed call.
+        scratch = torch.zeros(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        decode()  # evicts the zero fill's dirty lines before the first timed call
+        cold = []
+        for i in range(args.cold_steps):
+            sink = scratch.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            decode()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        rec["decode_us_cold"] = statistics.median(cold)
+        rec["kv_read_GBps_cold"] = nbytes["kv"] / (rec["decode_us_cold"] * 1e-6) / 1e9
+        del scratch, sink
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
