@@ -32,8 +32,11 @@
 // partial count.  merge_fast_kernel then merges the partials with log-sum-exp
 // in slot order and writes the rows of sequences without tiles.
 //
-// Block-table entries are fetched 64 at a time into a lane-indexed window and
-// picked out with readlane.  Tile buffers form a ring: the loads of tiles
+// Set-up per segment (up to 128 tiles and 8 pieces of units): one walk over
+// the segment's units writes a record per tile to LDS (element offset of the
+// tile in the pools, valid rows, first/last/bad flags) with all block-table
+// entries and q rows fetched by the lanes at once; the tile loop then reads
+// one LDS record per tile.  Tile buffers form a ring: the loads of tiles
 // t + 1 and t + 2 (t + 1 only, for G = 8) are in flight while tile t is
 // computed.
 #include <math.h>
@@ -152,17 +155,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int table_tokens = maxB * BS;
     const int32_t* __restrict__ ctxp = a.context_lens;
 
-    // ---- 1. total tiles
+    // ---- 1. total tiles.  The lengths of the first 512 sequences stay in
+    // registers (as tile counts) and in LDS, so for batches up to that size
+    // the search below and the unit walk read no more global memory.
+    __shared__ int ctx_lds[kWave * 8];
+    const bool lens_in_lds = S <= kWave * 8;
+    int nv0[8];
+    int s0 = 0;
     int total = 0;
     for (int base = 0; base < S; base += kWave * 8) {
         int s = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = base + lane * 8 + k;
-            if (i < S) s += tiles_of(ctxp[i], table_tokens);
+            const int c = i < S ? ctxp[i] : 0;
+            const int n = tiles_of(c, table_tokens);
+            if (base == 0) {
+                nv0[k] = n;
+                ctx_lds[lane * 8 + k] = c;
+            }
+            s += n;
         }
+        if (base == 0) s0 = s;
         total += wave_sum_int(s);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t Nt = (int64_t)total * Hkv;
     if (Nt == 0) return;
     const int W = (int)(Nt < nwaves ? Nt : nwaves);
@@ -178,11 +197,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int base = 0; base < S; base += kWave * 8) {
             int nv[8];
             int s = 0;
+            if (base == 0) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int i = base + lane * 8 + k;
-                nv[k] = i < S ? tiles_of(ctxp[i], table_tokens) : 0;
-                s += nv[k];
+                for (int k = 0; k < 8; ++k) nv[k] = nv0[k];
+                s = s0;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int i = base + lane * 8 + k;
+                    nv[k] = i < S ? tiles_of(ctxp[i], table_tokens) : 0;
+                    s += nv[k];
+                }
             }
             const int incl = wave_incl_scan_int(s, lane);
             const int64_t chunk = (int64_t)read_lane(incl, kWave - 1) * Hkv;
@@ -207,6 +232,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             acc += chunk;
         }
     }
+    // Length of sequence i (wave-uniform i).
+    auto len_of = [&](int i) -> int {
+        return lens_in_lds ? __builtin_amdgcn_readfirstlane(ctx_lds[i]) : ctxp[i];
+    };
     if (i0 < 0) return;  // unreachable when the two passes agree; keeps every index below in range
 
     const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
@@ -217,7 +246,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // Cursor at the next tile still to be placed in a segment.
     Cursor P;
     P.i = i0;
-    P.ctx = ctxp[i0];
+    P.ctx = len_of(i0);
     P.n = tiles_of(P.ctx, table_tokens);
     P.seq_base = base0;
     {
@@ -323,7 +352,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                     P.seq_base += (int64_t)Hkv * P.n;
                     do {
                         ++P.i;
-                        P.ctx = ctxp[P.i];
+                        P.ctx = len_of(P.i);
                         P.n = tiles_of(P.ctx, table_tokens);
                     } while (P.n == 0);
                 }
@@ -569,12 +598,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // outside the table).  Lanes own two output columns each.
 template <int G>
 __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, int table_tokens) {
+    constexpr int kFew = 8;  // partial counts handled with all loads in one round
     const int lane = threadIdx.x & (kWave - 1);
     const int h = threadIdx.x / kWave;
     const int64_t u = blockIdx.x;
     const int i = (int)(u / a.num_kv_heads);
     const int g = (int)(u % a.num_kv_heads);
+    // The record is read together with the length (it is garbage, and unused,
+    // when the sequence has no tiles).
     const int ctx = a.context_lens[i];
+    const int2 rec = a.ws_rec[u];
     float2* out = reinterpret_cast<float2*>(
         a.out + ((int64_t)i * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
     if (tiles_of(ctx, table_tokens) == 0) {
@@ -582,7 +615,6 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         *out = make_float2(v, v);
         return;
     }
-    const int2 rec = a.ws_rec[u];
     const int np = rec.y;
     if (np == 1) return;
     const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
@@ -591,6 +623,29 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         return;
     }
     const float2* ml = a.ws_ml + (int64_t)rec.x * G + h;
+    const float* acc = a.ws_acc + ((int64_t)rec.x * G + h) * kHd + 2 * lane;
+    const int64_t pstride = (int64_t)G * kHd;
+    if (np <= kFew) {
+        // lane p < np holds partial p's (m, l); every lane loads its two
+        // columns of all partials at once.
+        const float2 mlv = lane < np ? ml[(int64_t)lane * G] : make_float2(-INFINITY, 0.f);
+        float2 v[kFew];
+#pragma unroll
+        for (int p = 0; p < kFew; ++p)
+            v[p] = p < np ? *reinterpret_cast<const float2*>(acc + p * pstride) : make_float2(0.f, 0.f);
+        const float M = wave_max(mlv.x);
+        const float wgt = lane < np ? exp2f(mlv.x - M) : 0.f;
+        const float L = wave_sum(wgt * mlv.y);
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) {
+            const float wp = read_lane(wgt, p);
+            o0 = fmaf(wp, v[p].x, o0);
+            o1 = fmaf(wp, v[p].y, o1);
+        }
+        *out = make_float2(o0 / L, o1 / L);
+        return;
+    }
     float M = -INFINITY;
     for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[(int64_t)p * G].x);
     M = wave_max(M);
@@ -600,8 +655,6 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         L += exp2f(v.x - M) * v.y;
     }
     L = wave_sum(L);
-    const float* acc = a.ws_acc + ((int64_t)rec.x * G + h) * kHd + 2 * lane;
-    const int64_t pstride = (int64_t)G * kHd;
     float o0 = 0.f, o1 = 0.f;
     int p = 0;
     for (; p + 4 <= np; p += 4) {  // four partials' loads in flight at once
