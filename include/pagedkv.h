@@ -59,7 +59,9 @@ typedef enum pkv_status {
     PKV_ERR_UNSUPPORTED = 4, /* valid, but no kernel for this head_dim / block_size / group size */
     PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than paged_attn_workspace_bytes */
     PKV_ERR_HIP = 6,         /* the HIP runtime reported an error while enqueueing */
-    PKV_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned */
+    PKV_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned */
+    PKV_ERR_NO_BLOCKS = 8,   /* block manager: the pool has too few free blocks */
+    PKV_ERR_SEQ = 9          /* block manager: unknown, repeated or already existing sequence id */
 } pkv_status;
 
 typedef enum pkv_dtype {

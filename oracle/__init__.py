@@ -6,7 +6,8 @@ CPU-baseline leg of ``bench.py`` may import this package.  The product library
 library: the two share nothing but the seeded inputs from ``workloads``.
 
 ``oracle.c`` is plain C in fp64 (built with gcc, OpenMP over output rows);
-``arith.py`` holds the block and byte arithmetic.  Each function cites the
+``arith.py`` holds the block and byte arithmetic; ``blocks.py`` the block
+bookkeeping (allocation, sharing, copy-on-write) and the block copy.  Each function cites the
 passage of the pages it follows.
 """
 
@@ -21,6 +22,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import arith  # noqa: F401
+from . import blocks  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "oracle.c")

@@ -8,6 +8,8 @@ CPU or PyTorch fallback.
 
     paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache)
     out = paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale)
+    paged_block_copy(k_cache, v_cache, pairs)      # copy-on-write of whole blocks
+    BlockManager(num_blocks, block_size)           # host block manager (blocks.py)
 
 Layouts: pools ``[num_blocks][num_kv_heads][block_size][head_dim]`` (fp32 or
 bf16); ``q`` ``[num_seqs][num_q_heads][head_dim]`` of the pool dtype;
@@ -23,6 +25,7 @@ from typing import Dict, Optional, Tuple
 import torch
 
 from . import _lib
+from .blocks import BlockManager  # noqa: F401
 from ._lib import (  # noqa: F401
     KERNEL_NAMES,
     PKV_KERNEL_AUTO,
@@ -35,6 +38,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
+    "BlockManager",
+    "paged_block_copy",
     "paged_kv_write",
     "paged_attn_decode",
     "paged_attn_plan",
@@ -102,6 +107,20 @@ def paged_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch
         ctypes.c_void_p(slot_mapping.data_ptr()), T, ctypes.c_void_p(k_cache.data_ptr()),
         ctypes.c_void_p(v_cache.data_ptr()), ctypes.byref(desc), _stream(dev, stream))
     _lib.check(st, "paged_kv_write")
+
+
+def paged_block_copy(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks in both pools: block pairs[p][1] becomes block pairs[p][0], bit for bit."""
+    dev = k_cache.device
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (pairs, "pairs")):
+        _dev(t, n, dev)
+    desc = cache_desc(k_cache)
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache/v_cache differ")
+    _need(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2, "pairs must be int32 [n][2]")
+    st = _lib.lib().paged_block_copy(ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+                                     ctypes.c_void_p(pairs.data_ptr()), pairs.shape[0], ctypes.byref(desc),
+                                     _stream(dev, stream))
+    _lib.check(st, "paged_block_copy")
 
 
 def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,

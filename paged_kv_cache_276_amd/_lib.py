@@ -25,8 +25,20 @@ EXPORTS = (
     "paged_attn_plan",
     "paged_attn_workspace_bytes",
     "paged_attn_decode",
+    "paged_block_copy",
     "pkv_status_string",
     "pkv_version",
+    "pkv_bm_create",
+    "pkv_bm_destroy",
+    "pkv_bm_num_free",
+    "pkv_bm_refcount",
+    "pkv_bm_seq_len",
+    "pkv_bm_add",
+    "pkv_bm_fork",
+    "pkv_bm_free",
+    "pkv_bm_append",
+    "pkv_bm_slots",
+    "pkv_bm_block_tables",
 )
 
 
@@ -85,6 +97,31 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode.restype = ctypes.c_int
     L.paged_attn_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, ctypes.c_float, vp, vp, u64,
                                     P(CacheDesc), P(DecodeOpts), vp]
+    L.paged_block_copy.restype = ctypes.c_int
+    L.paged_block_copy.argtypes = [vp, vp, vp, i32, P(CacheDesc), vp]
+    i64 = ctypes.c_int64
+    L.pkv_bm_create.restype = ctypes.c_int
+    L.pkv_bm_create.argtypes = [i32, i32, P(vp)]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_destroy.argtypes = [vp]
+    L.pkv_bm_num_free.restype = i32
+    L.pkv_bm_num_free.argtypes = [vp]
+    L.pkv_bm_refcount.restype = i32
+    L.pkv_bm_refcount.argtypes = [vp, i32]
+    L.pkv_bm_seq_len.restype = i32
+    L.pkv_bm_seq_len.argtypes = [vp, i64]
+    L.pkv_bm_add.restype = ctypes.c_int
+    L.pkv_bm_add.argtypes = [vp, i64, i32]
+    L.pkv_bm_fork.restype = ctypes.c_int
+    L.pkv_bm_fork.argtypes = [vp, i64, i64]
+    L.pkv_bm_free.restype = ctypes.c_int
+    L.pkv_bm_free.argtypes = [vp, i64]
+    L.pkv_bm_append.restype = ctypes.c_int
+    L.pkv_bm_append.argtypes = [vp, vp, i32, vp, vp, i32, P(i32)]
+    L.pkv_bm_slots.restype = ctypes.c_int
+    L.pkv_bm_slots.argtypes = [vp, i64, i32, i32, vp]
+    L.pkv_bm_block_tables.restype = ctypes.c_int
+    L.pkv_bm_block_tables.argtypes = [vp, vp, i32, i32, vp, vp]
     L.pkv_status_string.restype = ctypes.c_char_p
     L.pkv_status_string.argtypes = [ctypes.c_int]
     L.pkv_version.restype = ctypes.c_char_p

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libpagedkv.so")
 
-SOURCES = ["kv_write.hip", "attn_generic.hip", "attn_fast.hip", "attn_combine.hip", "api.hip"]
+SOURCES = ["kv_write.hip", "attn_generic.hip", "attn_fast.hip", "attn_combine.hip", "api.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are kept out of the generated code on purpose.
@@ -38,7 +38,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -1,10 +1,11 @@
-// api.hip -- the extern "C" entry points of libpagedkv.so (declared in
-// include/pagedkv.h).  Host code only: argument validation, the launch plan,
+// api.hip -- the extern "C" device entry points of libpagedkv.so (declared in
+// include/pagedkv.h and include/pagedkv_blocks.h).  Host code only: argument validation, the launch plan,
 // and dispatch to the kernels.  Every check runs before anything is enqueued.
 #include <stdint.h>
 
 #include "launch.h"
 #include "pagedkv.h"
+#include "pagedkv_blocks.h"
 
 #define PKV_API extern "C" __attribute__((visibility("default")))
 
@@ -138,6 +139,22 @@ PKV_API pkv_status paged_kv_write(const void* k_new, const void* v_new, const in
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+PKV_API pkv_status paged_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                                    const pkv_cache_desc* cache, void* stream) {
+    pkv_status st = check_desc(cache);
+    if (st != PKV_OK) return st;
+    if (num_pairs < 0 || num_pairs > INT32_MAX / 2) return PKV_ERR_SHAPE;
+    if (!k_cache || !v_cache) return PKV_ERR_NULL;
+    if (num_pairs == 0) return PKV_OK;
+    if (!pairs) return PKV_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_ALIGN;
+    const int64_t elem = cache->dtype == PKV_BF16 ? 2 : 4;
+    const int64_t block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim * elem;
+    const hipError_t e = pkv::launch_block_copy(k_cache, v_cache, pairs, num_pairs, cache->num_blocks, block_bytes,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 PKV_API pkv_status paged_attn_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                    const pkv_cache_desc* cache, const pkv_decode_opts* opts,
                                    pkv_decode_plan* plan) {
@@ -223,6 +240,8 @@ PKV_API const char* pkv_status_string(pkv_status status) {
         case PKV_ERR_WORKSPACE: return "workspace missing or too small";
         case PKV_ERR_HIP: return "HIP runtime error while enqueueing";
         case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case PKV_ERR_NO_BLOCKS: return "not enough free blocks in the pool";
+        case PKV_ERR_SEQ: return "unknown, repeated or existing sequence id";
     }
     return "unknown status";
 }

@@ -52,4 +52,37 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* 
     return hipGetLastError();
 }
 
+// Whole-block copy inside both pools (copy-on-write of a shared block): one
+// workgroup row per pair, consecutive threads on consecutive 16-byte chunks of
+// the block (all KV heads, all slots), so reads and writes are contiguous.
+__global__ __launch_bounds__(256) void block_copy_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                         const int32_t* __restrict__ pairs, int64_t chunks_per_block,
+                                                         int32_t num_blocks) {
+    const int64_t p = blockIdx.x;
+    const int32_t src = pairs[2 * p];
+    const int32_t dst = pairs[2 * p + 1];
+    if ((uint32_t)src >= (uint32_t)num_blocks || (uint32_t)dst >= (uint32_t)num_blocks) return;
+    const int64_t so = (int64_t)src * chunks_per_block;
+    const int64_t d0 = (int64_t)dst * chunks_per_block;
+    for (int64_t j = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; j < chunks_per_block;
+         j += (int64_t)gridDim.y * blockDim.x) {
+        const uint4 kv = k_cache[so + j];
+        const uint4 vv = v_cache[so + j];
+        k_cache[d0 + j] = kv;
+        v_cache[d0 + j] = vv;
+    }
+}
+
+hipError_t launch_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                             int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    const int64_t chunks = block_bytes / 16;
+    const int threads = 256;
+    int64_t ys = (chunks + threads - 1) / threads;
+    if (ys > 16) ys = 16;
+    hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)num_pairs, (unsigned)ys), dim3(threads), 0, stream,
+                       static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs, chunks, num_blocks);
+    return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -40,6 +40,9 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* 
                            int32_t block_size, int32_t num_kv_heads, int32_t row_bytes,
                            hipStream_t stream);
 
+hipError_t launch_block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                             int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
 // Returns hipErrorInvalidValue when no instantiation matches the shape.
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);

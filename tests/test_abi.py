@@ -12,7 +12,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -27,10 +28,13 @@ def L():
 
 
 def _declared_functions():
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_\w+|pkv_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        with open(h) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(paged_\w+|pkv_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
@@ -46,7 +50,7 @@ def test_status_strings_and_version(L):
     from paged_kv_cache_276_amd import _lib
 
     assert _lib.status_string(0) == "ok"
-    for s in range(1, 8):
+    for s in range(1, 10):
         assert _lib.status_string(s) not in ("ok", "unknown status")
     assert _lib.status_string(99) == "unknown status"
     assert "gfx950" in L.pkv_version().decode()
@@ -181,3 +185,16 @@ def test_decode_validation_host_only(L):
     assert call(q=vp(0x10008)) == 7
     assert call(hq=12) == 2
     assert call(S=0) == 0              # nothing to do
+
+
+def test_block_copy_validation_host_only(L):
+    d = _desc()
+    vp = ctypes.c_void_p
+    fake = vp(0x10000)  # never dereferenced
+    assert L.paged_block_copy(fake, fake, fake, 0, ctypes.byref(d), None) == 0      # nothing to do
+    assert L.paged_block_copy(None, fake, fake, 1, ctypes.byref(d), None) == 1
+    assert L.paged_block_copy(fake, fake, None, 1, ctypes.byref(d), None) == 1
+    assert L.paged_block_copy(fake, fake, fake, -1, ctypes.byref(d), None) == 2
+    assert L.paged_block_copy(vp(0x10008), fake, fake, 1, ctypes.byref(d), None) == 7
+    bad = _desc(dtype=5)
+    assert L.paged_block_copy(fake, fake, fake, 1, ctypes.byref(bad), None) == 3
