@@ -52,6 +52,9 @@ def parse_args(argv=None):
                    help="after the timed steps, time this many decode calls each preceded by "
                         "reading --flush-mib of scratch (no KV bytes left in L2 or MALL)")
     p.add_argument("--flush-mib", type=int, default=512)
+    p.add_argument("--prefix", action="store_true",
+                   help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
+                        "each shared block is read once per group")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -67,14 +70,25 @@ def parse_args(argv=None):
 
 
 def algorithmic_bytes(w) -> dict:
+    """Bytes one decode call must move.  `kv` counts every sequence's tokens (the
+    logical attention input); `kv_unique` counts each physical block's used
+    tokens once (what a path that reads a shared block once per batch moves)."""
     ctx = w.context_lens.astype(np.int64)
     e = w.elem_bytes
     B = w.block_size
-    kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * e
+    per_token = 2 * w.num_kv_heads * w.head_dim * e
+    kv = int(ctx.sum()) * per_token
+    used = {}
+    for i, n in enumerate(ctx):
+        for b in range(-(-int(n) // B)):
+            phys = int(w.block_tables[i, b])
+            used[phys] = max(used.get(phys, 0), min(B, int(n) - b * B))
+    kv_unique = sum(used.values()) * per_token
     q = w.num_seqs * w.num_q_heads * w.head_dim * e
     out = w.num_seqs * w.num_q_heads * w.head_dim * 4
     tables = int(((ctx + B - 1) // B).sum()) * 4 + w.num_seqs * 4
-    return {"kv": kv, "q": q, "out": out, "tables": tables, "total": kv + q + out + tables}
+    return {"kv": kv, "kv_unique": kv_unique, "q": q, "out": out, "tables": tables,
+            "total": kv + q + out + tables, "total_unique": kv_unique + q + out + tables}
 
 
 def cpu_baseline(w) -> dict:
@@ -210,9 +224,30 @@ def main(argv=None) -> int:
         "context_lens": torch.from_numpy(w.context_lens).to(dev),
         "slot_mapping": torch.from_numpy(w.slot_mapping).to(dev),
     }
-    plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
-                               partition_tokens=args.partition_tokens, kernel=args.kernel,
-                               grid_waves=args.grid_waves)
+    if args.prefix:
+        groups = w.meta.get("prefix_groups")
+        if not groups:
+            print(json.dumps({"error": f"--prefix needs a workload with shared prefixes, not {args.config}"}))
+            return 2
+        start = np.zeros(w.num_seqs, dtype=np.int32)
+        grows = []
+        for ptok, members in groups:
+            start[members] = ptok
+            for k in range(0, len(members), 8):
+                grows.append((members[k], len(members[k:k + 8])))
+        d["seq_prefix"] = torch.from_numpy(start).to(dev)
+        d["groups"] = torch.from_numpy(np.array(grows, dtype=np.int32)).to(dev)
+        max_prefix = int(start.max())
+        plan = pkv.paged_attn_prefix_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, len(grows), max_prefix,
+                                          d["k_cache"], chunk_tokens=args.partition_tokens,
+                                          grid_waves=args.grid_waves)
+        plan["partition_tokens"] = plan["chunk_tokens"]
+        plan["grid_blocks"] = args.grid_waves
+        plan["kernel"] = "prefix"
+    else:
+        plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
+                                   partition_tokens=args.partition_tokens, kernel=args.kernel,
+                                   grid_waves=args.grid_waves)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = torch.empty((max(plan["workspace_bytes"], 16) + 15) // 16 * 16, dtype=torch.uint8, device=dev)
 
@@ -220,9 +255,14 @@ def main(argv=None) -> int:
         pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
 
     def decode():
-        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                              w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
-                              kernel=args.kernel, grid_waves=args.grid_waves)
+        if args.prefix:
+            pkv.paged_attn_decode_prefix(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                         d["seq_prefix"], d["groups"], max_prefix, w.scale, out=out, workspace=ws,
+                                         chunk_tokens=args.partition_tokens, grid_waves=args.grid_waves)
+        else:
+            pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                  w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
+                                  kernel=args.kernel, grid_waves=args.grid_waves)
 
     print(f"[bench] warmup {args.warmup} steps, plan {plan}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -248,7 +288,9 @@ def main(argv=None) -> int:
     decode_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
     dec_avg = statistics.mean(decode_ms)
     nbytes = algorithmic_bytes(w)
-    achieved = nbytes["total"] / (dec_avg * 1e-3) / 1e9
+    # The prefix path has to move each shared block once: it is priced on the unique bytes.
+    moved = nbytes["total_unique"] if args.prefix else nbytes["total"]
+    achieved = moved / (dec_avg * 1e-3) / 1e9
     kv_gbs = nbytes["kv"] / (dec_avg * 1e-3) / 1e9
 
     traffic = None
@@ -286,7 +328,8 @@ def main(argv=None) -> int:
             "grid_waves": plan["grid_blocks"],
         },
         "roofline": {
-            "kernel": "paged_attn_decode (partition + merge kernels, one call)",
+            "kernel": ("paged_attn_decode_prefix (prefix, suffix and merge kernels, one call; unique bytes)"
+                       if args.prefix else "paged_attn_decode (partition + merge kernels, one call)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
@@ -295,6 +338,7 @@ def main(argv=None) -> int:
             "traffic": traffic,
         },
         "kv_read_GBps": kv_gbs,
+        "kv_unique_GBps": nbytes["kv_unique"] / (dec_avg * 1e-3) / 1e9,
         "kv_read_pct_of_peak": 100.0 * kv_gbs / PEAK_HBM_GBS,
         "decode_us": dec_avg * 1e3,
         "decode_us_min": min(decode_ms) * 1e3,

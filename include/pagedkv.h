@@ -183,6 +183,60 @@ pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_c
                              const pkv_cache_desc *cache, const pkv_decode_opts *opts,
                              void *stream);
 
+/*
+ * paged_attn_prefix_plan -- host-only plan of paged_attn_decode_prefix: the
+ * fast kernel's plan with partition_tokens = tokens per prefix chunk,
+ * max_partitions = chunks of the longest prefix, workspace_bytes = the
+ * workspace paged_attn_decode_prefix needs.  Shapes as PKV_KERNEL_FAST
+ * (PKV_ERR_UNSUPPORTED otherwise).  opts->partition_tokens, if nonzero, sets
+ * the prefix chunk: a multiple of 16, at most 1024.
+ */
+pkv_status paged_attn_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                  int32_t num_groups, int32_t max_prefix_tokens,
+                                  const pkv_cache_desc *cache, const pkv_decode_opts *opts,
+                                  pkv_decode_plan *plan);
+
+/*
+ * paged_attn_decode_prefix -- the result of paged_attn_decode for a batch in
+ * which groups of sequences share the first blocks of their block tables
+ * (parallel samples of one prompt: page
+ * "praveentn.live/architecture/quiz/pagedattention-kv-cache-constraint",
+ * section "What the change bought").  Each shared block is read from HBM once
+ * per group and KV head rather than once per sequence: a prefix pass runs one
+ * wave per member over the group's prefix tiles held in LDS, the fast kernel
+ * covers each sequence's own tokens after its prefix, and a merge combines
+ * the pieces by log-sum-exp in token order.
+ *
+ *   seq_prefix_tokens (device) int32 [num_seqs]: tokens at the start of
+ *                 sequence i that its group shares, a whole number of blocks
+ *                 and at most context_lens[i]; 0 for a sequence in no group
+ *   groups       (device) int32 [num_groups][2]: first sequence and member
+ *                 count (1 .. 8) of each group.  Members are consecutive, have
+ *                 equal seq_prefix_tokens and the same first
+ *                 seq_prefix_tokens / block_size table entries (the first
+ *                 member's entries are read).
+ *   num_groups   (host) rows of `groups`; 0 is allowed (then every
+ *                 seq_prefix_tokens entry must be 0)
+ *   max_prefix_tokens (host) at least every seq_prefix_tokens entry, at most
+ *                 max_blocks_per_seq * block_size; sizes the prefix grid
+ * Everything else as paged_attn_decode; the workspace is
+ * paged_attn_prefix_plan's workspace_bytes (no initialisation needed).
+ *
+ * Device contents are not validated on the host.  A prefix that is not a
+ * whole number of blocks, longer than its sequence or than max_prefix_tokens,
+ * or that differs from its group's, gives NaN rows.  A sequence with a
+ * nonzero prefix that no group lists gives unspecified rows.  The kernels
+ * stay inside their buffers in every case.
+ */
+pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    const int32_t *seq_prefix_tokens, const int32_t *groups,
+                                    int32_t num_groups, int32_t max_prefix_tokens, float scale,
+                                    float *out, void *workspace, uint64_t workspace_bytes,
+                                    const pkv_cache_desc *cache, const pkv_decode_opts *opts,
+                                    void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *pkv_status_string(pkv_status status);
 

@@ -8,6 +8,8 @@ CPU or PyTorch fallback.
 
     paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache)
     out = paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale)
+    out = paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens,
+                                   seq_prefix_tokens, groups, max_prefix_tokens, scale)
     paged_block_copy(k_cache, v_cache, pairs)      # copy-on-write of whole blocks
     BlockManager(num_blocks, block_size)           # host block manager (blocks.py)
 
@@ -42,6 +44,8 @@ __all__ = [
     "paged_block_copy",
     "paged_kv_write",
     "paged_attn_decode",
+    "paged_attn_decode_prefix",
+    "paged_attn_prefix_plan",
     "paged_attn_plan",
     "paged_attn_workspace_bytes",
     "cache_desc",
@@ -213,4 +217,64 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         ctypes.c_void_p(context_lens.data_ptr()), S, Hq, ctypes.c_float(scale),
         ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes, ctypes.byref(desc), ctypes.byref(opts), s)
     _lib.check(st, "paged_attn_decode")
+    return out
+
+
+def paged_attn_prefix_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, num_groups: int,
+                           max_prefix_tokens: int, cache, chunk_tokens: int = 0, grid_waves: int = 0) -> Dict[str, int]:
+    """Host-only plan of the shared-prefix decode (prefix chunk, chunks, workspace bytes)."""
+    desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
+    plan = DecodePlan()
+    st = _lib.lib().paged_attn_prefix_plan(num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
+                                           max_prefix_tokens, ctypes.byref(desc),
+                                           ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)),
+                                           ctypes.byref(plan))
+    _lib.check(st, "paged_attn_prefix_plan")
+    return {"kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)), "chunk_tokens": plan.partition_tokens,
+            "max_chunks": plan.max_partitions, "workspace_bytes": plan.workspace_bytes}
+
+
+def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             seq_prefix_tokens: torch.Tensor, groups: torch.Tensor, max_prefix_tokens: int,
+                             scale: float, out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, chunk_tokens: int = 0,
+                             grid_waves: int = 0, stream=None) -> torch.Tensor:
+    """paged_attn_decode for groups of sequences sharing prefix blocks; each shared block is read once per group."""
+    dev = k_cache.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (seq_prefix_tokens, "seq_prefix_tokens"), (groups, "groups")):
+        _dev(t, n, dev)
+    desc = cache_desc(k_cache)
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache/v_cache differ")
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim and q.dtype == k_cache.dtype,
+          "q must be [S][Hq][D] of the cache dtype")
+    S, Hq = q.shape[0], q.shape[1]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be int32 [S][max_blocks_per_seq]")
+    for t, n in ((context_lens, "context_lens"), (seq_prefix_tokens, "seq_prefix_tokens")):
+        _need(t.dtype == torch.int32 and tuple(t.shape) == (S,), f"{n} must be int32 [S]")
+    _need(groups.dtype == torch.int32 and groups.dim() == 2 and groups.shape[1] == 2, "groups must be int32 [G][2]")
+    if out is None:
+        out = torch.empty((S, Hq, desc.head_dim), dtype=torch.float32, device=dev)
+    _dev(out, "out", dev)
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
+    maxb = block_tables.shape[1]
+    G = groups.shape[0]
+    plan = paged_attn_prefix_plan(S, Hq, maxb, G, max_prefix_tokens, desc, chunk_tokens, grid_waves)
+    s = _stream(dev, stream)
+    need = plan["workspace_bytes"]
+    if workspace is None:
+        workspace = _workspace(dev, int(s.value or 0), need)
+    else:
+        _dev(workspace, "workspace", dev)
+        _need(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
+    st = _lib.lib().paged_attn_decode_prefix(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), maxb, ctypes.c_void_p(context_lens.data_ptr()), S, Hq,
+        ctypes.c_void_p(seq_prefix_tokens.data_ptr()), ctypes.c_void_p(groups.data_ptr()), G,
+        int(max_prefix_tokens), ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), ctypes.byref(desc),
+        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)), s)
+    _lib.check(st, "paged_attn_decode_prefix")
     return out

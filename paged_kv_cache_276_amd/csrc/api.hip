@@ -196,7 +196,7 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
         plan.kernel == PKV_KERNEL_FAST ? fast_layout(num_seqs, cache->num_kv_heads, group, cache->head_dim)
                                        : generic_layout(num_seqs, num_q_heads, plan.max_partitions, cache->head_dim);
     char* ws = static_cast<char*>(workspace);
-    pkv::DecodeArgs a;
+    pkv::DecodeArgs a{};
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
@@ -227,6 +227,130 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
         e = pkv::launch_decode_generic(a, s);
         if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
     }
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+namespace {
+
+// Shared-prefix path: the fast plan plus the chunking of the prefixes and the
+// chunk partials after the fast workspace.
+struct PrefixPlan {
+    pkv_decode_plan base;      // fast plan of the suffix pass
+    int32_t chunk_tiles;       // 16-token tiles per prefix chunk
+    int32_t max_chunks;        // chunks of the longest prefix
+    WorkspaceLayout fast;      // suffix pass workspace
+    uint64_t pml_bytes, pacc_bytes;
+    uint64_t total;
+};
+
+constexpr int32_t kPrefixChunkTilesMax = 64;
+constexpr int64_t kPrefixTargetWorkgroups = 1024;
+
+pkv_status make_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                            int32_t num_groups, int32_t max_prefix_tokens, const pkv_cache_desc* cache,
+                            const pkv_decode_opts* opts, PrefixPlan* pp) {
+    pkv_decode_opts o = opts ? *opts : pkv_decode_opts{0, PKV_KERNEL_AUTO, 0};
+    const int32_t chunk_tokens = o.partition_tokens;
+    o.partition_tokens = 0;
+    o.kernel = PKV_KERNEL_FAST;
+    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &pp->base);
+    if (st != PKV_OK) return st;
+    if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
+    if (num_groups < 0 || max_prefix_tokens < 0) return PKV_ERR_SHAPE;
+    if ((int64_t)max_prefix_tokens > (int64_t)max_blocks_per_seq * cache->block_size) return PKV_ERR_SHAPE;
+    if (cache->num_kv_heads > 65535) return PKV_ERR_SHAPE;
+    const int64_t prefix_tiles = (max_prefix_tokens + 15) / 16;
+    int64_t ct;
+    if (chunk_tokens) {
+        if (chunk_tokens < 0 || chunk_tokens % 16 != 0 || chunk_tokens / 16 > kPrefixChunkTilesMax) return PKV_ERR_SHAPE;
+        ct = chunk_tokens / 16;
+    } else {
+        // about kPrefixTargetWorkgroups workgroups for the whole prefix pass
+        ct = (prefix_tiles * num_groups * cache->num_kv_heads + kPrefixTargetWorkgroups - 1) / kPrefixTargetWorkgroups;
+        ct = ct < 8 ? 8 : (ct > kPrefixChunkTilesMax ? kPrefixChunkTilesMax : ct);
+    }
+    const int64_t mc = (prefix_tiles + ct - 1) / ct;
+    if (mc > 65535) return PKV_ERR_SHAPE;
+    const int32_t group = num_q_heads / cache->num_kv_heads;
+    pp->chunk_tiles = (int32_t)ct;
+    pp->max_chunks = num_groups ? (int32_t)mc : 0;
+    pp->fast = fast_layout(num_seqs, cache->num_kv_heads, group, cache->head_dim);
+    const uint64_t rows = (uint64_t)num_seqs * cache->num_kv_heads * (uint64_t)pp->max_chunks * group;
+    pp->pml_bytes = align_up(rows * sizeof(float2), 256);
+    pp->pacc_bytes = rows * (uint64_t)cache->head_dim * sizeof(float);
+    pp->total = align_up(pp->fast.total, 256) + pp->pml_bytes + pp->pacc_bytes;
+    pp->base.partition_tokens = (int32_t)ct * 16;
+    pp->base.max_partitions = pp->max_chunks;
+    pp->base.workspace_bytes = pp->total;
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_API pkv_status paged_attn_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          int32_t num_groups, int32_t max_prefix_tokens,
+                                          const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                                          pkv_decode_plan* plan) {
+    if (!plan) return PKV_ERR_NULL;
+    PrefixPlan pp;
+    const pkv_status st = make_prefix_plan(num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
+                                           max_prefix_tokens, cache, opts, &pp);
+    if (st == PKV_OK) *plan = pp.base;
+    return st;
+}
+
+PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                            const int32_t* seq_prefix_tokens, const int32_t* groups,
+                                            int32_t num_groups, int32_t max_prefix_tokens, float scale,
+                                            float* out, void* workspace, uint64_t workspace_bytes,
+                                            const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                                            void* stream) {
+    PrefixPlan pp;
+    pkv_status st = make_prefix_plan(num_seqs, num_q_heads, max_blocks_per_seq, num_groups, max_prefix_tokens,
+                                     cache, opts, &pp);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !seq_prefix_tokens) return PKV_ERR_NULL;
+    if (num_groups > 0 && !groups) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_ERR_ALIGN;
+    if (!workspace || workspace_bytes < pp.total) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+
+    char* ws = static_cast<char*>(workspace);
+    const WorkspaceLayout& wl = pp.fast;
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_blocks = cache->num_blocks;
+    a.block_size = cache->block_size;
+    a.head_dim = cache->head_dim;
+    a.dtype = cache->dtype;
+    a.scale = scale;
+    a.out = out;
+    a.ws_rec = reinterpret_cast<int2*>(ws);
+    a.ws_ml = reinterpret_cast<float2*>(ws + wl.rec_bytes);
+    a.ws_acc = reinterpret_cast<float*>(ws + wl.rec_bytes + wl.ml_bytes);
+    a.part_tokens = 16;
+    a.max_parts = pkv::kMaxGridWaves;
+    a.grid_waves = opts ? opts->grid_waves : 0;
+    a.seq_start = seq_prefix_tokens;
+    a.groups = groups;
+    a.num_groups = num_groups;
+    a.prefix_chunk_tiles = pp.chunk_tiles;
+    a.prefix_max_chunks = pp.max_chunks;
+    const uint64_t poff = align_up(wl.total, 256);
+    a.ws_pml = reinterpret_cast<float2*>(ws + poff);
+    a.ws_pacc = reinterpret_cast<float*>(ws + poff + pp.pml_bytes);
+    const hipError_t e = pkv::launch_decode_prefix(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -47,72 +47,15 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "tile_math.h"
 
 namespace pkv {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kTok = 16;              // tokens per tile
-constexpr int kHd = 128;              // head_dim of this path
-constexpr float kLazyRescale = 8.0f;  // log2 units the running max may trail the tile max
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// All-reduce within each 16-lane row (row_ror 8, 4, 2, 1).
-__device__ __forceinline__ float row_max16(float v) {
-    v = fmaxf(v, dpp_f<0x128>(v));
-    v = fmaxf(v, dpp_f<0x124>(v));
-    v = fmaxf(v, dpp_f<0x122>(v));
-    v = fmaxf(v, dpp_f<0x121>(v));
-    return v;
-}
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp_f<0x128>(v);
-    v += dpp_f<0x124>(v);
-    v += dpp_f<0x122>(v);
-    v += dpp_f<0x121>(v);
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan_int(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {
-    return (ctx < 0 || ctx > table_tokens) ? 0 : (ctx + kTok - 1) / kTok;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-// Wait for every outstanding vector-memory load (vmcnt 0; expcnt and lgkmcnt
-// left at their maxima).  Placed at the end of the rare branches that load
-// (block-table refill, a unit's q) so the common path's waits count only the
-// tile loads and the next tile stays in flight.
-__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 2^x with the hardware instruction alone (no denormal-range fix-up: softmax
-// weights below 2^-126 flush to zero, far below the fp32 accumulation error).
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 struct Cursor {
     int i;             // sequence
+    int start;         // first token of the sequence this kernel covers (0 without a shared prefix)
     int g;             // KV head
     int b;             // tile within the (sequence, KV head) unit
     int n;             // tiles of the unit
@@ -133,7 +76,10 @@ constexpr uint32_t kBad = 1u << 18;    // block-table entry outside the pool
 
 }  // namespace
 
-template <int BS, int G>
+// START: every sequence i covers tokens [seq_start[i], ctx) only (the tokens
+// before are a shared prefix handled by decode_prefix_kernel), and no unit is
+// finished here: all of them leave partial results for the merge.
+template <int BS, int G, bool START>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(const DecodeArgs a,
                                                                                                   float qscale) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -159,7 +105,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // registers (as tile counts) and in LDS, so for batches up to that size
     // the search below and the unit walk read no more global memory.
     __shared__ int ctx_lds[kWave * 8];
+    __shared__ int start_lds[START ? kWave * 8 : 1];
     const bool lens_in_lds = S <= kWave * 8;
+    const int32_t* __restrict__ startp = a.seq_start;
+    auto tiles_at = [&](int c, int st) { return START ? tiles_from(c, st, table_tokens) : tiles_of(c, table_tokens); };
     int nv0[8];
     int s0 = 0;
     int total = 0;
@@ -169,10 +118,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int k = 0; k < 8; ++k) {
             const int i = base + lane * 8 + k;
             const int c = i < S ? ctxp[i] : 0;
-            const int n = tiles_of(c, table_tokens);
+            const int st = (START && i < S) ? startp[i] : 0;
+            const int n = tiles_at(c, st);
             if (base == 0) {
                 nv0[k] = n;
                 ctx_lds[lane * 8 + k] = c;
+                if (START) start_lds[lane * 8 + k] = st;
             }
             s += n;
         }
@@ -205,7 +156,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = base + lane * 8 + k;
-                    nv[k] = i < S ? tiles_of(ctxp[i], table_tokens) : 0;
+                    nv[k] = i < S ? tiles_at(ctxp[i], START ? startp[i] : 0) : 0;
                     s += nv[k];
                 }
             }
@@ -236,6 +187,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     auto len_of = [&](int i) -> int {
         return lens_in_lds ? __builtin_amdgcn_readfirstlane(ctx_lds[i]) : ctxp[i];
     };
+    auto start_of = [&](int i) -> int {
+        if (!START) return 0;
+        return lens_in_lds ? __builtin_amdgcn_readfirstlane(start_lds[i]) : startp[i];
+    };
     if (i0 < 0) return;  // unreachable when the two passes agree; keeps every index below in range
 
     const uint16_t* __restrict__ qbase = static_cast<const uint16_t*>(a.q);
@@ -247,7 +202,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     Cursor P;
     P.i = i0;
     P.ctx = len_of(i0);
-    P.n = tiles_of(P.ctx, table_tokens);
+    P.start = start_of(i0);
+    P.n = tiles_at(P.ctx, P.start);
     P.seq_base = base0;
     {
         const int64_t off = c0 - base0;
@@ -274,7 +230,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float m[4], l[4];
     bool bad = false, from_start = false;
     int ui = 0, ug = 0, un = 1;  // unit being accumulated
-    int64_t useq_base = 0;
+    int useq_base = 0;           // global index of its sequence's first tile
+    int ustart = 0;              // first token of its sequence covered here
 
     // Leave the current unit: write its output (the wave saw every tile of it)
     // or a partial result at slot unit + wave; the wave that saw the unit's
@@ -293,7 +250,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
         const int64_t u = (int64_t)ui * Hkv + ug;
-        if (from_start && unit_end) {
+        if (from_start && unit_end && !(START && ustart != 0)) {
             if (lane < 16) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
@@ -323,7 +280,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             if (lane == h) a.ws_ml[slot * G + h] = make_float2(mh, bad ? NAN : lh);
         }
         if (from_start && lane == 0) {
-            const int64_t last_tile = useq_base + (int64_t)ug * un + un - 1;
+            const int64_t last_tile = (int64_t)useq_base + (int64_t)ug * un + un - 1;
             const int64_t w_last = ((last_tile + 1) * W - 1) / Nt;
             a.ws_rec[u] = make_int2((int)slot, (int)(w_last - w + 1));
         }
@@ -339,8 +296,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const int len = min(P.n - P.b, room - k);
             if (lane == 0) {
                 run_lds[nruns][0] = make_int4(P.i, P.g, P.n, P.b);
-                run_lds[nruns][1] = make_int4((int)(uint32_t)P.seq_base,
-                                              (int)(uint32_t)((uint64_t)P.seq_base >> 32), k, P.ctx);
+                run_lds[nruns][1] = make_int4((int)P.seq_base, P.start, k, P.ctx);
             }
             k += len;
             ++nruns;
@@ -353,7 +309,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                     do {
                         ++P.i;
                         P.ctx = len_of(P.i);
-                        P.n = tiles_of(P.ctx, table_tokens);
+                        P.start = start_of(P.i);
+                        P.n = tiles_at(P.ctx, P.start);
                     } while (P.n == 0);
                 }
             }
@@ -388,8 +345,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 if (j >= run_lds[q][1].z) r = q;
             trun[half] = r;
             const int4 d = run_lds[r][0];
-            const int b = d.w + (j - run_lds[r][1].z);
-            phys[half] = j < seg_len ? bt[(int64_t)d.x * maxB + (b * kTok) / BS] : 0;
+            const int4 e = run_lds[r][1];
+            const int b = d.w + (j - e.z);
+            phys[half] = j < seg_len ? bt[(int64_t)d.x * maxB + (e.y + b * kTok) / BS] : 0;
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -399,7 +357,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const int4 d = run_lds[r][0];
                 const int4 e = run_lds[r][1];
                 const int b = d.w + (j - e.z);
-                const int tok0 = b * kTok;
+                const int tok0 = e.y + b * kTok;
                 const bool badp = (unsigned)phys[half] >= (unsigned)a.num_blocks;
                 const int ph = badp ? 0 : phys[half];
                 const int64_t off = (((int64_t)ph * Hkv + d.y) * BS + (tok0 % BS)) * kHd;
@@ -450,8 +408,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 ui = __builtin_amdgcn_readfirstlane(r0.x);
                 ug = __builtin_amdgcn_readfirstlane(r0.y);
                 un = __builtin_amdgcn_readfirstlane(r0.z);
-                useq_base = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(r1.y) << 32) |
-                                      (uint32_t)__builtin_amdgcn_readfirstlane(r1.x));
+                useq_base = __builtin_amdgcn_readfirstlane(r1.x);
+                ustart = __builtin_amdgcn_readfirstlane(r1.y);
                 const uint16_t* qrow = reinterpret_cast<const uint16_t*>(&q_lds[r][0]);
 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) {
@@ -596,7 +554,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // and out = sum_p 2^(m_p - M) acc_p / L over the unit's partials in slot
 // order.  Sequences without tiles get zero rows (empty) or NaN rows (length
 // outside the table).  Lanes own two output columns each.
-template <int G>
+// PREFIX: the unit also has the chunk partials of its group's shared prefix
+// (tokens [0, seq_start[i]), from decode_prefix_kernel); they come first in
+// the merge order, then the unit's own partials, and the partition kernel
+// finished none of these units itself.
+template <int G, bool PREFIX>
 __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, int table_tokens) {
     constexpr int kFew = 8;  // partial counts handled with all loads in one round
     const int lane = threadIdx.x & (kWave - 1);
@@ -605,34 +567,49 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
     const int i = (int)(u / a.num_kv_heads);
     const int g = (int)(u % a.num_kv_heads);
     // The record is read together with the length (it is garbage, and unused,
-    // when the sequence has no tiles).
+    // when the sequence has no tiles here).
     const int ctx = a.context_lens[i];
+    const int st = PREFIX ? a.seq_start[i] : 0;
     const int2 rec = a.ws_rec[u];
     float2* out = reinterpret_cast<float2*>(
         a.out + ((int64_t)i * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
-    if (tiles_of(ctx, table_tokens) == 0) {
-        const float v = ctx == 0 ? 0.f : NAN;
-        *out = make_float2(v, v);
-        return;
-    }
-    const int np = rec.y;
-    if (np == 1) return;
-    const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
-    if (np < 1 || rec.x < 0 || (int64_t)rec.x + np > slots) {  // never written: refuse to read
+    const bool valid = st >= 0 && st <= ctx && ctx <= table_tokens && (st & (kTok - 1)) == 0;
+    const int ns = PREFIX ? tiles_from(ctx, st, table_tokens) : tiles_of(ctx, table_tokens);
+    const int npc = (PREFIX && st > 0) ? (st / kTok + a.prefix_chunk_tiles - 1) / a.prefix_chunk_tiles : 0;
+    if (!valid || npc > (PREFIX ? a.prefix_max_chunks : 0)) {
         *out = make_float2(NAN, NAN);
         return;
     }
-    const float2* ml = a.ws_ml + (int64_t)rec.x * G + h;
-    const float* acc = a.ws_acc + ((int64_t)rec.x * G + h) * kHd + 2 * lane;
-    const int64_t pstride = (int64_t)G * kHd;
+    if (ns == 0 && npc == 0) {  // empty sequence
+        *out = make_float2(0.f, 0.f);
+        return;
+    }
+    const int nps = ns > 0 ? rec.y : 0;
+    if (npc == 0 && nps == 1) return;  // finished by the partition kernel
+    const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
+    if (ns > 0 && (nps < 1 || rec.x < 0 || (int64_t)rec.x + nps > slots)) {  // never written: refuse to read
+        *out = make_float2(NAN, NAN);
+        return;
+    }
+    const int np = npc + nps;
+    const int64_t prow = u * (PREFIX ? a.prefix_max_chunks : 0);
+    // Partial p: prefix chunk p, then the unit's slots in order.
+    auto ml_of = [&](int p) -> float2 {
+        if (PREFIX && p < npc) return a.ws_pml[(prow + p) * G + h];
+        return a.ws_ml[((int64_t)rec.x + p - npc) * G + h];
+    };
+    auto acc_of = [&](int p) -> float2 {
+        const float* base = (PREFIX && p < npc) ? a.ws_pacc + ((prow + p) * G + h) * kHd
+                                                : a.ws_acc + (((int64_t)rec.x + p - npc) * G + h) * kHd;
+        return *reinterpret_cast<const float2*>(base + 2 * lane);
+    };
     if (np <= kFew) {
         // lane p < np holds partial p's (m, l); every lane loads its two
         // columns of all partials at once.
-        const float2 mlv = lane < np ? ml[(int64_t)lane * G] : make_float2(-INFINITY, 0.f);
+        const float2 mlv = lane < np ? ml_of(lane) : make_float2(-INFINITY, 0.f);
         float2 v[kFew];
 #pragma unroll
-        for (int p = 0; p < kFew; ++p)
-            v[p] = p < np ? *reinterpret_cast<const float2*>(acc + p * pstride) : make_float2(0.f, 0.f);
+        for (int p = 0; p < kFew; ++p) v[p] = p < np ? acc_of(p) : make_float2(0.f, 0.f);
         const float M = wave_max(mlv.x);
         const float wgt = lane < np ? exp2f(mlv.x - M) : 0.f;
         const float L = wave_sum(wgt * mlv.y);
@@ -647,11 +624,11 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         return;
     }
     float M = -INFINITY;
-    for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[(int64_t)p * G].x);
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml_of(p).x);
     M = wave_max(M);
     float L = 0.f;
     for (int p = lane; p < np; p += kWave) {
-        const float2 v = ml[(int64_t)p * G];
+        const float2 v = ml_of(p);
         L += exp2f(v.x - M) * v.y;
     }
     L = wave_sum(L);
@@ -661,8 +638,8 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         float2 v[4], mlv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[k] = *reinterpret_cast<const float2*>(acc + (p + k) * pstride);
-            mlv[k] = ml[(int64_t)(p + k) * G];
+            v[k] = acc_of(p + k);
+            mlv[k] = ml_of(p + k);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -672,12 +649,232 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
         }
     }
     for (; p < np; ++p) {
-        const float2 v = *reinterpret_cast<const float2*>(acc + p * pstride);
-        const float wgt = exp2f(ml[(int64_t)p * G].x - M);
+        const float2 v = acc_of(p);
+        const float wgt = exp2f(ml_of(p).x - M);
         o0 = fmaf(wgt, v.x, o0);
         o1 = fmaf(wgt, v.y, o1);
     }
     *out = make_float2(o0 / L, o1 / L);
+}
+
+// Shared-prefix chunk partials.  Workgroup (group k, KV head g, chunk c) runs
+// one wave per member sequence of the group (at most kPrefixWaves).  The
+// group's prefix, tokens [0, P) named by the first member's block table, is
+// read once per workgroup: every 16-token tile of the chunk is loaded into LDS
+// by all the workgroup's threads (kPrefixAhead tiles in flight), then each
+// wave applies the tile step of decode_fast_kernel to its own sequence's G
+// query heads (MFMA scores, online softmax, P.V in fp32), reading K and V from
+// LDS.  Each wave leaves the chunk's (m, l, acc) of its sequence for the merge.
+constexpr int kPrefixWaves = kPrefixGroupMax;
+constexpr int kPrefixAhead = 4;           // tiles in flight per workgroup
+constexpr int kPrefixChunkTilesMax = 64;  // LDS table size
+constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes): conflict-free fragment reads
+
+template <int BS, int G>
+__global__ __launch_bounds__(64 * kPrefixWaves) void decode_prefix_kernel(const DecodeArgs a, float qscale) {
+    constexpr int ROWS = (G + 3) / 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid / kWave;
+    const int k = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
+    const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int maxB = a.max_blocks_per_seq;
+    const int table_tokens = maxB * BS;
+    const int CT = a.prefix_chunk_tiles;
+
+    const int first = a.groups[2 * k];
+    const int count = a.groups[2 * k + 1];
+    if (first < 0 || count < 1 || count > kPrefixWaves || first > S - count) return;  // uniform
+    const int P = a.seq_start[first];
+    const bool p_ok = P > 0 && P % BS == 0 && P <= table_tokens;
+    const int nt_total = p_ok ? P / kTok : 0;
+    const int t0 = c * CT;
+    const int t1 = min(t0 + CT, nt_total);
+    const int ntile = max(t1 - t0, 0);
+
+    // This wave's sequence and whether it writes chunk c.
+    const bool member = wv < count;
+    const int i = member ? first + wv : first;
+    const int st = a.seq_start[i];
+    const int ctx = a.context_lens[i];
+    const int npc = st > 0 ? (st / kTok + CT - 1) / CT : 0;
+    const bool writes = member && c < npc;
+    bool bad = !(p_ok && st == P && ctx >= P && ctx <= table_tokens);
+
+    __shared__ uint2 toff_lds[kPrefixChunkTilesMax];  // element offset of each tile (lo, hi)
+    __shared__ int tbad_lds[kPrefixChunkTilesMax];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
+    __shared__ uint4 v_lds[2][kTok * kHd / 8];
+    __shared__ float4 p_lds[kPrefixWaves][16 * ROWS];
+
+    const int32_t* __restrict__ bt = a.block_tables;
+    if (tid < ntile) {
+        const int tok0 = (t0 + tid) * kTok;
+        const int phys = bt[(int64_t)first * maxB + tok0 / BS];
+        const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
+        const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * kHd;
+        toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
+        tbad_lds[tid] = badp;
+    }
+    // q rows of this wave's sequence in the MFMA A layout (rows >= G are zero)
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    uint4 qc[4];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)i * Hq + (int64_t)g * G + (r16 < G ? r16 : 0)) * kHd;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
+            qc[kq] = r16 < G ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    // Thread tid moves 16 bytes of each tile: K rows for tid < 256, V rows otherwise.
+    const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_cache);
+    const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_cache);
+    const bool is_k = tid < kTok * kHd / 8;
+    const int part = is_k ? tid : tid - kTok * kHd / 8;
+    auto load_tile = [&](int j) -> uint4 {
+        const uint2 o = toff_lds[j];
+        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x);
+        const uint16_t* src = (is_k ? kbase : vbase) + off + part * 8;
+        return *reinterpret_cast<const uint4*>(src);
+    };
+    auto store_tile = [&](int buf, const uint4& v) {
+        if (is_k) {
+            *reinterpret_cast<uint4*>(&k_lds[buf][(part >> 4) * kKRow + (part & 15) * 16]) = v;
+        } else {
+            v_lds[buf][part] = v;
+        }
+    };
+
+    float acc[G][8];
+    float m[4], l[4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+    }
+
+    // One tile from LDS buffer `buf` for this wave's rows.
+    auto step = [&](int buf, int j) {
+        bad = bad || tbad_lds[j] != 0;
+        uint4 kf[4];
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            kf[kq] = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kq]), as_bf16x8(kf[kq]), sc, 0, 0, 0);
+        float s[4];
+        bool need = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = sc[r] * qscale;
+            need = need || (s[r] > m[r] + kLazyRescale);
+        }
+        if (__any(need && lane < 16 * ROWS)) {
+            float alpha[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float tm = row_max16(s[r]);
+                const float mn = tm > m[r] + kLazyRescale ? tm : m[r];
+                alpha[r] = fast_exp2(m[r] - mn);
+                m[r] = mn;
+                l[r] *= alpha[r];
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float ah = read_lane(alpha[h & 3], 16 * (h >> 2));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = fast_exp2(s[r] - m[r]);
+            l[r] += p[r];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        if (lane < 16 * ROWS) p_lds[wv][lane] = make_float4(p[0], p[1], p[2], p[3]);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int trow = 4 * ii + grp;
+            float pw[8];
+            const float4 p0 = p_lds[wv][trow];
+            pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
+            if (G == 8) {
+                const float4 p1 = p_lds[wv][16 + trow];
+                pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
+            }
+            const uint4 u = v_lds[buf][trow * (kHd / 8) + r16];
+            float vv[8];
+            vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
+            vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
+            vv[4] = bf16_lo(u.z); vv[5] = bf16_hi(u.z);
+            vv[6] = bf16_lo(u.w); vv[7] = bf16_hi(u.w);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], vv[e], acc[h][e]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Tiles j = 0 .. ntile-1 of the chunk; R[j % kPrefixAhead] holds tile j's
+    // 16 bytes from its load until it is stored to LDS buffer j % 2.
+    uint4 R[kPrefixAhead];
+#pragma unroll
+    for (int q = 0; q < kPrefixAhead; ++q) R[q] = q < ntile ? load_tile(q) : make_uint4(0, 0, 0, 0);
+    for (int j0 = 0; j0 < ntile; j0 += kPrefixAhead) {
+#pragma unroll
+        for (int q = 0; q < kPrefixAhead; ++q) {
+            const int j = j0 + q;
+            if (j < ntile) {  // uniform
+                store_tile(j & 1, R[q]);
+                if (j + kPrefixAhead < ntile) R[q] = load_tile(j + kPrefixAhead);
+                __syncthreads();
+                if (writes && !bad) step(j & 1, j);
+            }
+        }
+    }
+
+    if (!writes) return;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
+            acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
+        }
+    float lsum[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
+    const int64_t prow = ((int64_t)i * Hkv + g) * a.prefix_max_chunks + c;
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float4* pa = reinterpret_cast<float4*>(a.ws_pacc + (prow * G + h) * kHd + 8 * lane);
+            pa[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            pa[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
+        const float mh = read_lane(m[h & 3], 16 * (h >> 2));
+        if (lane == h) a.ws_pml[prow * G + h] = make_float2(mh, bad ? NAN : lh);
+    }
 }
 
 namespace {
@@ -704,26 +901,40 @@ int resident_waves(const void* kernel) {
 }
 
 template <int BS, int G>
+hipError_t launch_prefix_chunks(const DecodeArgs& a, hipStream_t stream) {
+    if (a.num_groups == 0 || a.prefix_max_chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.num_groups, (unsigned)a.num_kv_heads, (unsigned)a.prefix_max_chunks);
+    hipLaunchKernelGGL((decode_prefix_kernel<BS, G>), grid, dim3(kWave * kPrefixWaves), 0, stream, a,
+                       a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+template <int BS, int G, bool PREFIX>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-    const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G>);
+    if (PREFIX) {
+        const hipError_t e = launch_prefix_chunks<BS, G>(a, stream);
+        if (e != hipSuccess) return e;
+    }
+    const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G, PREFIX>);
     int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
     if (waves <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_fast_kernel<BS, G>), dim3(waves), dim3(kWave), 0, stream, a, a.scale * kLog2e);
+    hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX>), dim3(waves), dim3(kWave), 0, stream, a,
+                       a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
-    hipLaunchKernelGGL((merge_fast_kernel<G>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
+    hipLaunchKernelGGL((merge_fast_kernel<G, PREFIX>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
                        a.max_blocks_per_seq * BS);
     return hipGetLastError();
 }
 
-template <int BS>
+template <int BS, bool PREFIX>
 hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_t<BS, 1>(a, stream);
-        case 2: return launch_t<BS, 2>(a, stream);
-        case 4: return launch_t<BS, 4>(a, stream);
-        case 8: return launch_t<BS, 8>(a, stream);
+        case 1: return launch_t<BS, 1, PREFIX>(a, stream);
+        case 2: return launch_t<BS, 2, PREFIX>(a, stream);
+        case 4: return launch_t<BS, 4, PREFIX>(a, stream);
+        case 8: return launch_t<BS, 8, PREFIX>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -738,9 +949,18 @@ bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t 
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
     switch (a.block_size) {
-        case 16: return by_group<16>(a, stream);
-        case 32: return by_group<32>(a, stream);
-        case 64: return by_group<64>(a, stream);
+        case 16: return by_group<16, false>(a, stream);
+        case 32: return by_group<32, false>(a, stream);
+        case 64: return by_group<64, false>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs& a, hipStream_t stream) {
+    switch (a.block_size) {
+        case 16: return by_group<16, true>(a, stream);
+        case 32: return by_group<32, true>(a, stream);
+        case 64: return by_group<64, true>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

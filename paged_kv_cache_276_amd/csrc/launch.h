@@ -31,6 +31,14 @@ struct DecodeArgs {
     int32_t part_tokens;
     int32_t max_parts;
     int32_t grid_waves;  // fast kernel: requested waves (0 = resident capacity)
+    // Shared-prefix path (paged_attn_decode_prefix); zero/null otherwise.
+    const int32_t* seq_start;    // [S] tokens of each sequence covered by its group's shared prefix
+    const int32_t* groups;       // [num_groups][2] first sequence, member count
+    int32_t num_groups;
+    int32_t prefix_chunk_tiles;  // 16-token tiles per prefix chunk
+    int32_t prefix_max_chunks;   // chunk partials kept per (sequence, KV head)
+    float2* ws_pml;              // prefix partials (m, l): [S][Hkv][max_chunks][G]
+    float* ws_pacc;              // prefix partials acc: [S][Hkv][max_chunks][G][head_dim]
 };
 
 constexpr int32_t kMaxGridWaves = 8192;  // PKV_MAX_GRID_WAVES
@@ -46,6 +54,9 @@ hipError_t launch_block_copy(void* k_cache, void* v_cache, const int32_t* pairs,
 // Returns hipErrorInvalidValue when no instantiation matches the shape.
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
+// Shared-prefix decode: prefix kernel, suffix tiles (fast kernel), merge.
+hipError_t launch_decode_prefix(const DecodeArgs& a, hipStream_t stream);
+constexpr int32_t kPrefixGroupMax = 8;  // sequences per prefix group (one wave each)
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 
 bool generic_supports(int32_t dtype, int32_t head_dim, int32_t group);

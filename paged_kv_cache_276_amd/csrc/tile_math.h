@@ -1,0 +1,75 @@
+// tile_math.h -- wave-level helpers shared by the bf16 / head_dim 128 decode
+// kernels (attn_fast.hip, attn_prefix.hip): MFMA operand types, 16-lane row
+// reductions, wave scans and the tile constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTok = 16;              // tokens per tile
+constexpr int kHd = 128;              // head_dim of this path
+constexpr float kLazyRescale = 8.0f;  // log2 units the running max may trail the tile max
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// All-reduce within each 16-lane row (row_ror 8, 4, 2, 1).
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp_f<0x128>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x122>(v));
+    v = fmaxf(v, dpp_f<0x121>(v));
+    return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp_f<0x128>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x122>(v);
+    v += dpp_f<0x121>(v);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(v, d, kWave);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {
+    return (ctx < 0 || ctx > table_tokens) ? 0 : (ctx + kTok - 1) / kTok;
+}
+
+// Tiles of tokens [start, ctx) of a sequence; 0 when the pair is not valid
+// (start outside [0, ctx] or not a whole number of tiles, ctx past the table).
+__device__ __forceinline__ int tiles_from(int ctx, int start, int table_tokens) {
+    return (start < 0 || start > ctx || ctx > table_tokens || (start & (kTok - 1)) != 0)
+               ? 0
+               : (ctx - start + kTok - 1) / kTok;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 2^x with the hardware instruction alone (no denormal-range fix-up: softmax
+// weights below 2^-126 flush to zero, far below the fp32 accumulation error).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace
+}  // namespace pkv

@@ -1,0 +1,159 @@
+"""GPU parity of the shared-prefix decode (paged_attn_decode_prefix) against the oracle.
+
+The oracle knows nothing of prefixes: it rebuilds every sequence's K/V from its
+own block table and evaluates plain attention, so agreement shows that reading
+each shared block once per group (page
+"praveentn.live/architecture/quiz/pagedattention-kv-cache-constraint", section
+"What the change bought") changes no result beyond rounding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_276_amd as pkv
+from gpu_util import assert_parity, bits, say, set_key, to_device
+from workloads import make_config, make_custom
+
+pytestmark = pytest.mark.gpu
+
+
+def prefix_args(w, dev, split=8):
+    """seq_prefix_tokens [S], groups [G][2] (at most `split` members each) and the longest prefix."""
+    S = w.num_seqs
+    start = np.zeros(S, dtype=np.int32)
+    groups = []
+    for p, members in w.meta.get("prefix_groups", []):
+        members = sorted(members)
+        assert members == list(range(members[0], members[0] + len(members))), "members must be consecutive"
+        for m in members:
+            start[m] = p
+        for k in range(0, len(members), split):
+            chunk = members[k:k + split]
+            groups.append((chunk[0], len(chunk)))
+    g = np.array(groups, dtype=np.int32).reshape(-1, 2)
+    return (torch.from_numpy(start).to(dev), torch.from_numpy(g).to(dev), int(start.max(initial=0)))
+
+
+def run_prefix(w, d=None, write=True, chunk_tokens=0, grid_waves=0, split=8, start_override=None):
+    d = d or to_device(w)
+    dev = d["q"].device
+    if write:
+        pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    start, groups, maxp = prefix_args(w, dev, split)
+    if start_override is not None:
+        start = torch.from_numpy(np.asarray(start_override, dtype=np.int32)).to(dev)
+        maxp = max(maxp, int(start.max()))
+    out = pkv.paged_attn_decode_prefix(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                       start, groups, maxp, w.scale, chunk_tokens=chunk_tokens,
+                                       grid_waves=grid_waves)
+    torch.cuda.synchronize()
+    return d, out
+
+
+def _check(w, oracle_impl, what, **kw):
+    say(f"[gpu] prefix {what}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} B={w.block_size} {kw}")
+    d, out = run_prefix(w, **kw)
+    ref = oracle.decode_step(w, oracle=oracle_impl)
+    assert np.array_equal(bits(d["k_cache"]), ref.k_cache_bits)
+    ratio = assert_parity(out, ref.out, what)
+    say(f"[gpu] prefix {what}: ok, worst err/allowed {ratio:.4f}")
+    return out
+
+
+def test_shared_prefix_workload(oracle_impl):
+    """The 32 prompts x 8 samples workload at full size, and chunk sizes around the default."""
+    w = make_config("shared_prefix")
+    for ct in (0, 256, 1024):
+        _check(w, oracle_impl, f"shared_prefix/chunk{ct}", chunk_tokens=ct)
+
+
+CASES = [
+    # lengths, Hq, Hkv, B, prefix groups (tokens, members)
+    ([100, 130, 97, 200], 8, 2, 16, [(96, [0, 1, 2, 3])]),
+    ([33, 34, 35, 36, 37, 38, 39, 40, 41], 4, 4, 32, [(32, [0, 1, 2, 3, 4, 5, 6, 7])]),  # 8 members + 1 alone
+    ([1100, 1025, 1500, 700, 65, 80], 16, 2, 64, [(1024, [0, 1, 2]), (64, [4, 5])]),      # G = 8; seq 3 alone
+    ([300, 310], 2, 2, 16, [(288, [0, 1])]),                                             # G = 1
+    ([600] * 5 + [40] * 3, 8, 4, 32, [(576, [0, 1, 2, 3, 4]), (32, [5, 6, 7])]),          # G = 2
+    ([4097, 4100, 4200, 5000], 8, 2, 16, [(4096, [0, 1, 2, 3])]),                         # many chunks
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_prefix_cases(case, oracle_impl):
+    lens, hq, hkv, B, groups = CASES[case]
+    w = make_custom(lens, hq, hkv, 128, B, torch.bfloat16, seed=100 + case, prefix_groups=groups, pool_fill=0.7)
+    for ct in (0, 16, 64):
+        for waves in (0, 8):
+            _check(w, oracle_impl, f"case{case}/ct{ct}/w{waves}", chunk_tokens=ct, grid_waves=waves)
+
+
+def test_groups_split_in_eights(oracle_impl):
+    """A prompt with 20 samples is described as groups of 8, 8 and 4."""
+    w = make_custom([530 + 7 * i for i in range(20)], 8, 2, 128, 16, torch.bfloat16, seed=9,
+                    prefix_groups=[(512, list(range(20)))])
+    _check(w, oracle_impl, "split20", split=8)
+    _check(w, oracle_impl, "split20by3", split=3)
+
+
+def test_prefix_needles(oracle_impl):
+    """A dominant key in the prefix (first, middle, last token, chunk edges) and in the suffix."""
+    B, P = 32, 1024
+    positions = [0, 31, 32, 255, 256, 511, 512, P - 1, P, P + 40]
+    n = P + 64
+    # needles differ per sequence, so each sequence is a group of one (the prefix pass still covers
+    # its first P tokens)
+    w = make_custom([n] * len(positions), 8, 2, 128, B, torch.bfloat16, seed=23,
+                    prefix_groups=[(P, [i]) for i in range(len(positions))])
+    for i, pos in enumerate(positions):
+        q = w.q[i, 0].float()
+        c = 20.0 / (w.scale * float(q @ q))
+        set_key(w, i, pos, 0, c * q)
+    out = _check(w, oracle_impl, "needles", chunk_tokens=256)
+    for i, pos in enumerate(positions):
+        v = w.v_cache[int(w.block_tables[i, pos // B]), 0, pos % B].float()
+        assert torch.allclose(out[i, 0].cpu(), v, atol=0.05), (i, pos)
+
+
+def test_prefix_matches_plain_decode_and_is_placement_free():
+    """The prefix path agrees with paged_attn_decode, and is bit-identical under a second placement."""
+    w1 = make_custom([700, 650, 690, 800, 20], 8, 2, 128, 32, torch.bfloat16, seed=77,
+                     prefix_groups=[(640, [0, 1, 2, 3])], pool_fill=0.6)
+    w2 = make_custom([700, 650, 690, 800, 20], 8, 2, 128, 32, torch.bfloat16, seed=77,
+                     prefix_groups=[(640, [0, 1, 2, 3])], pool_fill=0.6)
+    rng = np.random.default_rng(3)
+    used = sorted({int(p) for p in w1.block_tables.reshape(-1) if p >= 0})
+    perm = rng.permutation(w1.num_blocks)
+    new_of = {old: int(perm[k]) for k, old in enumerate(used)}
+    for c1, c2 in ((w1.k_cache, w2.k_cache), (w1.v_cache, w2.v_cache)):
+        c2.copy_(torch.full_like(c1, float("nan")))
+        for old, new in new_of.items():
+            c2[new] = c1[old]
+    w2.block_tables = np.where(w1.block_tables >= 0,
+                               np.vectorize(lambda p: new_of.get(int(p), -1))(w1.block_tables), -1).astype(np.int32)
+    B = w1.block_size
+    w2.slot_mapping = np.array([new_of[int(s) // B] * B + int(s) % B for s in w1.slot_mapping], dtype=np.int32)
+    _, o1 = run_prefix(w1, chunk_tokens=128)
+    _, o2 = run_prefix(w2, chunk_tokens=128)
+    assert torch.equal(o1, o2)
+    d = to_device(w1)
+    pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+    plain = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"], w1.scale)
+    torch.cuda.synchronize()
+    assert torch.allclose(o1, plain, atol=2e-3, rtol=1e-2)
+
+
+def test_malformed_prefixes_give_nan_rows():
+    """A prefix that is not whole blocks, or longer than its sequence or the bound, turns rows NaN (no over-read)."""
+    w = make_custom([200, 210, 220, 90, 300], 8, 2, 128, 32, torch.bfloat16, seed=5,
+                    prefix_groups=[(192, [0, 1, 2])], pool_fill=0.7)
+    start = [192, 192, 192, 0, 0]
+    _, good = run_prefix(w, start_override=start)
+    assert torch.isfinite(good).all()
+    bad_start = [192, 176, 192, 96, 0]  # seq 1 disagrees with its group (not whole blocks), seq 3 past its length
+    _, out = run_prefix(w, start_override=bad_start)
+    assert torch.isnan(out[1]).all() and torch.isnan(out[3]).all()
+    # the other rows are unaffected (the suffix split over waves moves with the tile count, so not bit for bit)
+    for i in (0, 2, 4):
+        assert torch.allclose(out[i], good[i], atol=1e-6, rtol=1e-5), i

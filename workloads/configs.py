@@ -197,6 +197,8 @@ def _build(
 
     scale = float(np.float32(1.0 / math.sqrt(D)))
     m = {"used_blocks": used, "pool_fill": used / pool_blocks}
+    if prefix_groups:
+        m["prefix_groups"] = [(int(p), [int(i) for i in members]) for p, members in prefix_groups]
     if meta:
         m.update(meta)
     return Workload(
