@@ -119,7 +119,7 @@ def cpu_baseline(w) -> dict:
     }
 
 
-DECODE_KERNELS = ("decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel")
+DECODE_KERNELS = ("decode_prefix_kernel", "decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel")
 
 
 def _counter_rows(run_dir: str):

@@ -244,7 +244,7 @@ struct PrefixPlan {
 };
 
 constexpr int32_t kPrefixChunkTilesMax = 64;
-constexpr int64_t kPrefixTargetWorkgroups = 1024;
+constexpr int64_t kPrefixTargetWorkgroups = 512;  // about two per CU of the largest parts
 
 pkv_status make_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                             int32_t num_groups, int32_t max_prefix_tokens, const pkv_cache_desc* cache,

@@ -657,22 +657,35 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
     *out = make_float2(o0 / L, o1 / L);
 }
 
-// Shared-prefix chunk partials.  Workgroup (group k, KV head g, chunk c) runs
-// one wave per member sequence of the group (at most kPrefixWaves).  The
-// group's prefix, tokens [0, P) named by the first member's block table, is
-// read once per workgroup: every 16-token tile of the chunk is loaded into LDS
-// by all the workgroup's threads (kPrefixAhead tiles in flight), then each
-// wave applies the tile step of decode_fast_kernel to its own sequence's G
-// query heads (MFMA scores, online softmax, P.V in fp32), reading K and V from
-// LDS.  Each wave leaves the chunk's (m, l, acc) of its sequence for the merge.
-constexpr int kPrefixWaves = kPrefixGroupMax;
+// Shared-prefix chunk partials.  Workgroup (group k, KV head g, chunk c) has
+// four waves.  The group's prefix, tokens [0, P) named by the first member's
+// block table, is read once per workgroup: every 16-token tile of the chunk is
+// loaded into LDS by all 256 threads (kPrefixAhead tiles in flight), K as
+// stored and V transposed (dims x tokens).  The group's query rows -- member
+// m's heads g*G .. g*G+G-1 as rows m*G .. m*G+G-1, at most 64 -- are dealt 16
+// per wave, so the matrix cores see no padding unless the group is small:
+//   * S^T = K Q^T by four v_mfma_f32_16x16x32_bf16 (A = the 16 key rows, B =
+//     the wave's 16 query rows), which leaves lane l the scores of row l % 16
+//     for tokens 4 (l / 16) .. + 3;
+//   * online softmax per row in log2 units (lazy max as in decode_fast_kernel;
+//     the row's four lane groups agree on its max);
+//   * P V by v_mfma_f32_16x16x16bf16_1k: the scores' layout is already the A
+//     operand; P is split into a bf16 high part and a bf16 remainder (two
+//     MFMAs each), so every product is exact and the sums are fp32; B = V^T
+//     from LDS; the accumulator holds 16 rows x 128 dims in 32 registers.
+// Each row's (m, l, acc) for chunk c goes to its member's partial slot.
+constexpr int kPrefixWaves = 4;
+constexpr int kPrefixThreads = kPrefixWaves * 64;
 constexpr int kPrefixAhead = 4;           // tiles in flight per workgroup
 constexpr int kPrefixChunkTilesMax = 64;  // LDS table size
 constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes): conflict-free fragment reads
+constexpr int kVtRow = kTok * 2;          // LDS row of the transposed V tile (one dim, 16 tokens)
+static_assert(kPrefixGroupMax * 8 <= 16 * kPrefixWaves, "rows of a full group at G = 8 fit the waves");
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int BS, int G>
-__global__ __launch_bounds__(64 * kPrefixWaves) void decode_prefix_kernel(const DecodeArgs a, float qscale) {
-    constexpr int ROWS = (G + 3) / 4;
+__global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const DecodeArgs a, float qscale) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -684,28 +697,20 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void decode_prefix_kernel(const 
 
     const int first = a.groups[2 * k];
     const int count = a.groups[2 * k + 1];
-    if (first < 0 || count < 1 || count > kPrefixWaves || first > S - count) return;  // uniform
+    if (first < 0 || count < 1 || count > kPrefixGroupMax || first > S - count) return;  // uniform
     const int P = a.seq_start[first];
     const bool p_ok = P > 0 && P % BS == 0 && P <= table_tokens;
     const int nt_total = p_ok ? P / kTok : 0;
     const int t0 = c * CT;
     const int t1 = min(t0 + CT, nt_total);
     const int ntile = max(t1 - t0, 0);
-
-    // This wave's sequence and whether it writes chunk c.
-    const bool member = wv < count;
-    const int i = member ? first + wv : first;
-    const int st = a.seq_start[i];
-    const int ctx = a.context_lens[i];
-    const int npc = st > 0 ? (st / kTok + CT - 1) / CT : 0;
-    const bool writes = member && c < npc;
-    bool bad = !(p_ok && st == P && ctx >= P && ctx <= table_tokens);
+    const int rows = count * G;
+    const bool computes = 16 * wv < rows;  // wave-uniform
 
     __shared__ uint2 toff_lds[kPrefixChunkTilesMax];  // element offset of each tile (lo, hi)
     __shared__ int tbad_lds[kPrefixChunkTilesMax];
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
-    __shared__ uint4 v_lds[2][kTok * kHd / 8];
-    __shared__ float4 p_lds[kPrefixWaves][16 * ROWS];
+    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][kHd * kVtRow];
 
     const int32_t* __restrict__ bt = a.block_tables;
     if (tid < ntile) {
@@ -716,164 +721,173 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void decode_prefix_kernel(const 
         toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
         tbad_lds[tid] = badp;
     }
-    // q rows of this wave's sequence in the MFMA A layout (rows >= G are zero)
+    // The wave's query rows as the B operand of S^T = K Q^T (rows past the group are zero).
     const int r16 = lane & 15;
     const int grp = lane >> 4;
     uint4 qc[4];
     {
-        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)i * Hq + (int64_t)g * G + (r16 < G ? r16 : 0)) * kHd;
+        const int r = 16 * wv + r16;
+        const bool real = r < rows;
+        const int mi = first + (real ? r / G : 0);
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(a.q) + ((int64_t)mi * Hq + (int64_t)g * G + (real ? r % G : 0)) * kHd;
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
             const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
-            qc[kq] = r16 < G ? v : make_uint4(0, 0, 0, 0);
+            qc[kq] = real ? v : make_uint4(0, 0, 0, 0);
         }
     }
     __syncthreads();
 
-    // Thread tid moves 16 bytes of each tile: K rows for tid < 256, V rows otherwise.
-    const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.k_cache);
-    const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.v_cache);
-    const bool is_k = tid < kTok * kHd / 8;
-    const int part = is_k ? tid : tid - kTok * kHd / 8;
-    auto load_tile = [&](int j) -> uint4 {
+    // Thread tid takes dims 2j, 2j+1 (j = tid % 64) of tokens 4 (tid / 64) .. + 3
+    // of both K and V: eight 4-byte loads, each 256 contiguous bytes per wave.
+    // Every thread issues the same loads, so the waits for the tiles
+    // kPrefixAhead ahead stay exact.  K is stored as it is (padded rows), V
+    // transposed.
+    const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
+    const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
+    const int vtg = tid >> 6, vj = tid & 63;
+    struct TileKV {
+        uint4 k, v;
+    };
+    auto load_tile = [&](int j) -> TileKV {
         const uint2 o = toff_lds[j];
-        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x);
-        const uint16_t* src = (is_k ? kbase : vbase) + off + part * 8;
-        return *reinterpret_cast<const uint4*>(src);
+        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)(4 * vtg) * (kHd / 2) + vj;
+        TileKV t;
+        t.k = make_uint4(k32[off], k32[off + kHd / 2], k32[off + 2 * (kHd / 2)], k32[off + 3 * (kHd / 2)]);
+        t.v = make_uint4(v32[off], v32[off + kHd / 2], v32[off + 2 * (kHd / 2)], v32[off + 3 * (kHd / 2)]);
+        return t;
     };
-    auto store_tile = [&](int buf, const uint4& v) {
-        if (is_k) {
-            *reinterpret_cast<uint4*>(&k_lds[buf][(part >> 4) * kKRow + (part & 15) * 16]) = v;
-        } else {
-            v_lds[buf][part] = v;
-        }
+    auto store_tile = [&](int buf, const TileKV& t) {
+        unsigned char* kb = &k_lds[buf][(4 * vtg) * kKRow + 4 * vj];
+        *reinterpret_cast<uint32_t*>(kb) = t.k.x;
+        *reinterpret_cast<uint32_t*>(kb + kKRow) = t.k.y;
+        *reinterpret_cast<uint32_t*>(kb + 2 * kKRow) = t.k.z;
+        *reinterpret_cast<uint32_t*>(kb + 3 * kKRow) = t.k.w;
+        const uint4 v = t.v;
+        const uint2 even = make_uint2((v.x & 0xffffu) | (v.y << 16), (v.z & 0xffffu) | (v.w << 16));
+        const uint2 odd = make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj) * kVtRow + 8 * vtg]) = even;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj + 1) * kVtRow + 8 * vtg]) = odd;
     };
 
-    float acc[G][8];
-    float m[4], l[4];
+    f32x4 acc[kHd / 16];  // rows 4 grp .. + 3 of the wave, dims 16 jb + r16
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m[r] = -INFINITY;
-        l[r] = 0.f;
-    }
+    for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;  // running max of row r16 (the same in its four lane groups)
+    float l = 0.f;        // this lane's part of row r16's softmax denominator
+    bool bad = false;     // a block-table entry outside the pool
 
-    // One tile from LDS buffer `buf` for this wave's rows.
     auto step = [&](int buf, int j) {
         bad = bad || tbad_lds[j] != 0;
-        uint4 kf[4];
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-            kf[kq] = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qc[kq]), as_bf16x8(kf[kq]), sc, 0, 0, 0);
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qc[kq]), sc, 0, 0, 0);
+        }
         float s[4];
         bool need = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             s[r] = sc[r] * qscale;
-            need = need || (s[r] > m[r] + kLazyRescale);
+            need = need || (s[r] > m + kLazyRescale);
         }
-        if (__any(need && lane < 16 * ROWS)) {
-            float alpha[4];
+        if (__any(need)) {
+            float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+            const float mn = tm > m + kLazyRescale ? tm : m;
+            const float alpha = fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float tm = row_max16(s[r]);
-                const float mn = tm > m[r] + kLazyRescale ? tm : m[r];
-                alpha[r] = fast_exp2(m[r] - mn);
-                m[r] = mn;
-                l[r] *= alpha[r];
-            }
+                const float ar = __shfl(alpha, 4 * grp + r, kWave);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float ah = read_lane(alpha[h & 3], 16 * (h >> 2));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+                for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
             }
         }
-        float p[4];
+        s16x4 phi, plo;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = fast_exp2(s[r] - m[r]);
-            l[r] += p[r];
+            const float pr = fast_exp2(s[r] - m);
+            l += pr;
+            const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
+            phi[r] = (short)(hb >> 16);
+            plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (lane < 16 * ROWS) p_lds[wv][lane] = make_float4(p[0], p[1], p[2], p[3]);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int trow = 4 * ii + grp;
-            float pw[8];
-            const float4 p0 = p_lds[wv][trow];
-            pw[0] = p0.x; pw[1] = p0.y; pw[2] = p0.z; pw[3] = p0.w;
-            if (G == 8) {
-                const float4 p1 = p_lds[wv][16 + trow];
-                pw[4] = p1.x; pw[5] = p1.y; pw[6] = p1.z; pw[7] = p1.w;
-            }
-            const uint4 u = v_lds[buf][trow * (kHd / 8) + r16];
-            float vv[8];
-            vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
-            vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
-            vv[4] = bf16_lo(u.z); vv[5] = bf16_hi(u.z);
-            vv[6] = bf16_lo(u.w); vv[7] = bf16_hi(u.w);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h], vv[e], acc[h][e]);
+        for (int jb = 0; jb < kHd / 16; ++jb) {
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * jb + r16) * kVtRow + 8 * grp]);
+            const s16x4 vv = __builtin_bit_cast(s16x4, vb);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
     };
 
-    // Tiles j = 0 .. ntile-1 of the chunk; R[j % kPrefixAhead] holds tile j's
-    // 16 bytes from its load until it is stored to LDS buffer j % 2.
-    uint4 R[kPrefixAhead];
+    // Loads past the last tile fetch the last tile again (unused), so every
+    // iteration issues the same loads.
+    TileKV R[kPrefixAhead];
+    if (ntile > 0) {
 #pragma unroll
-    for (int q = 0; q < kPrefixAhead; ++q) R[q] = q < ntile ? load_tile(q) : make_uint4(0, 0, 0, 0);
-    for (int j0 = 0; j0 < ntile; j0 += kPrefixAhead) {
+        for (int q = 0; q < kPrefixAhead; ++q) R[q] = load_tile(min(q, ntile - 1));
+    }
+    // Full groups of kPrefixAhead tiles (no branch around the loads), then the
+    // remaining tiles, whose loads were issued by the last group.
+    int j0 = 0;
+    for (; j0 + kPrefixAhead <= ntile; j0 += kPrefixAhead) {
 #pragma unroll
         for (int q = 0; q < kPrefixAhead; ++q) {
             const int j = j0 + q;
-            if (j < ntile) {  // uniform
-                store_tile(j & 1, R[q]);
-                if (j + kPrefixAhead < ntile) R[q] = load_tile(j + kPrefixAhead);
-                __syncthreads();
-                if (writes && !bad) step(j & 1, j);
-            }
+            store_tile(j & 1, R[q]);
+            R[q] = load_tile(min(j + kPrefixAhead, ntile - 1));
+            __syncthreads();
+            if (computes) step(j & 1, j);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kPrefixAhead - 1; ++q) {
+        const int j = j0 + q;
+        if (j < ntile) {  // uniform
+            store_tile(j & 1, R[q]);
+            __syncthreads();
+            if (computes) step(j & 1, j);
         }
     }
 
-    if (!writes) return;
+    if (!computes) return;
+    float lt = l + __shfl_xor(l, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    // Row r of the wave is member r / G, head r % G.  A member writes chunk c
+    // when its own prefix has that chunk; its rows are NaN when its prefix
+    // disagrees with the group's or does not fit its sequence.
+    auto row_state = [&](int r, int64_t& prow, bool& rbad) -> bool {
+        if (r >= rows) return false;
+        const int mi = first + r / G;
+        const int st = a.seq_start[mi];
+        const int npc = st > 0 ? (st / kTok + CT - 1) / CT : 0;
+        if (c >= npc) return false;
+        const int ctx = a.context_lens[mi];
+        rbad = bad || !(p_ok && st == P && ctx >= P && ctx <= table_tokens);
+        prow = ((int64_t)mi * Hkv + g) * a.prefix_max_chunks + c;
+        return true;
+    };
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * wv + 4 * grp + rr;
+        int64_t prow;
+        bool rbad;
+        if (row_state(r, prow, rbad)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
-            acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
-        }
-    float lsum[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
-    const int64_t prow = ((int64_t)i * Hkv + g) * a.prefix_max_chunks + c;
-    if (lane < 16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float4* pa = reinterpret_cast<float4*>(a.ws_pacc + (prow * G + h) * kHd + 8 * lane);
-            pa[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-            pa[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+            for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[(prow * G + r % G) * kHd + 16 * jb + r16] = acc[jb][rr];
         }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
-        const float mh = read_lane(m[h & 3], 16 * (h >> 2));
-        if (lane == h) a.ws_pml[prow * G + h] = make_float2(mh, bad ? NAN : lh);
+    if (lane < 16) {
+        const int r = 16 * wv + lane;
+        int64_t prow;
+        bool rbad;
+        if (row_state(r, prow, rbad)) a.ws_pml[prow * G + r % G] = make_float2(m, rbad ? NAN : lt);
     }
 }
 
@@ -904,7 +918,7 @@ template <int BS, int G>
 hipError_t launch_prefix_chunks(const DecodeArgs& a, hipStream_t stream) {
     if (a.num_groups == 0 || a.prefix_max_chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)a.num_groups, (unsigned)a.num_kv_heads, (unsigned)a.prefix_max_chunks);
-    hipLaunchKernelGGL((decode_prefix_kernel<BS, G>), grid, dim3(kWave * kPrefixWaves), 0, stream, a,
+    hipLaunchKernelGGL((decode_prefix_kernel<BS, G>), grid, dim3(kPrefixThreads), 0, stream, a,
                        a.scale * kLog2e);
     return hipGetLastError();
 }
