@@ -52,6 +52,8 @@ def parse_args(argv=None):
                    help="after the timed steps, time this many decode calls each preceded by "
                         "reading --flush-mib of scratch (no KV bytes left in L2 or MALL)")
     p.add_argument("--flush-mib", type=int, default=512)
+    p.add_argument("--block-size", type=int, default=0,
+                   help="redraw the workload's lengths into blocks of this many tokens (block-size sweep)")
     p.add_argument("--prefix", action="store_true",
                    help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
                         "each shared block is read once per group")
@@ -216,7 +218,7 @@ def main(argv=None) -> int:
 
     dev = torch.device("cuda", 0)
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
-    w = make_config(args.config)
+    w = make_config(args.config, block_size=args.block_size or None)
     d = {
         "q": w.q.to(dev), "k_new": w.k_new.to(dev), "v_new": w.v_new.to(dev),
         "k_cache": w.k_cache.to(dev), "v_cache": w.v_cache.to(dev),
@@ -297,7 +299,7 @@ def main(argv=None) -> int:
     if os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             t = json.load(f)
-        key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}"
+        key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}" + (f"/B{w.block_size}" if args.block_size else "")
         if key in t and t[key].get("source_sha") == _kernel_source_sha():
             traffic = t[key]["bytes_per_launch"]
 
@@ -323,6 +325,9 @@ def main(argv=None) -> int:
             "block_size": w.block_size,
             "context_tokens": int(w.context_lens.sum()),
             "lengths": w.meta.get("lengths", "fixed"),
+            "slack_tokens": int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum()
+                                * w.block_size - w.context_lens.astype(np.int64).sum()),
+            "table_entries": int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum()),
             "kernel": plan["kernel"],
             "partition_tokens": plan["partition_tokens"],
             "grid_waves": plan["grid_blocks"],
@@ -383,7 +388,7 @@ def main(argv=None) -> int:
         import oracle
         from workloads import make_config as _mk
 
-        fresh = _mk(args.config)  # pre-write state; the GPU pool has been written K+W times (same slots)
+        fresh = _mk(args.config, block_size=args.block_size or None)  # pre-write state; the pool was rewritten K+W times (same slots)
         ref = oracle.decode_step(fresh)
         g = out.double().cpu().numpy()
         err = np.abs(g - ref.out)

@@ -258,3 +258,11 @@ def test_workspace_errors_raise():
         pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                               w.scale, workspace=torch.empty(16, dtype=torch.uint8, device=d["q"].device),
                               partition_tokens=64)
+
+
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+def test_block_size_sweep(B, oracle_impl):
+    """The batch-256 lengths redrawn into blocks of B tokens (the block-size sweep), 48 sequences."""
+    w = make_config("hc_b256", num_seqs=48, block_size=B)
+    for k in _kernels_for(w):
+        _check_step(w, oracle_impl, f"blocksize{B}/k{k}", kernel=k)

@@ -226,12 +226,15 @@ def _build(
 
 
 def make_config(name: str, poison: bool = True, num_seqs: Optional[int] = None,
-                values: bool = True) -> Workload:
+                values: bool = True, block_size: Optional[int] = None) -> Workload:
     """One of the five named workloads.
 
     ``num_seqs`` trims the batch (used only to draw a bounded sample of a
     workload; the full configuration is ``num_seqs=None``).  The lengths of the
     first ``num_seqs`` sequences are the same as in the full draw.
+    ``block_size`` redraws the same lengths into blocks of that many tokens (the
+    block-size sweep); the table width is scaled to keep the same token
+    capacity, and shared prefixes must stay whole blocks.
     """
     seed = _SEEDS[name]
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -268,6 +271,12 @@ def make_config(name: str, poison: bool = True, num_seqs: Optional[int] = None,
         meta = {"lengths": "2048 shared + uniform [1,512]", "prompts": prompts, "samples": samples}
     else:
         raise KeyError(name)
+    if block_size is not None and block_size != kw["block_size"]:
+        cap = kw["max_blocks_per_seq"] * kw["block_size"]
+        kw["block_size"] = block_size
+        kw["max_blocks_per_seq"] = -(-cap // block_size)
+        kw.pop("pool_blocks", None)
+        meta = dict(meta, block_size_sweep=block_size)
     if num_seqs is not None and num_seqs < len(lengths):
         lengths = lengths[:num_seqs]
         if "prefix_groups" in kw:
