@@ -85,9 +85,32 @@ class Oracle:
         self.lib.oracle_kv_write.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32]
         self.lib.oracle_num_threads.restype = ctypes.c_int
         self.lib.oracle_num_threads.argtypes = []
+        self.lib.oracle_attn_multi.restype = ctypes.c_int
+        self.lib.oracle_attn_multi.argtypes = [
+            vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp]
         self.lib.oracle_attn_decode.restype = ctypes.c_int
         self.lib.oracle_attn_decode.argtypes = [
             vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, i32, vp]
+
+    def attn_multi(self, q, k_cache, v_cache, block_tables, context_lens, cu_q, scale: float,
+                   num_kv_heads: Optional[int] = None) -> np.ndarray:
+        """fp64 causal attention of several new tokens per sequence.  Returns [total_q][Hq][D]."""
+        qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+        tq, hq, d = qb.shape
+        nb, hkv, b, d2 = kb.shape
+        assert d2 == d and vb.shape == kb.shape and qb.dtype.itemsize == kb.dtype.itemsize
+        if num_kv_heads is not None:
+            assert num_kv_heads == hkv
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        cu = np.ascontiguousarray(cu_q, dtype=np.int32)
+        s = bt.shape[0]
+        assert cl.shape == (s,) and cu.shape == (s + 1,) and int(cu[-1]) == tq
+        out = np.zeros((tq, hq, d), dtype=np.float64)
+        self._check(self.lib.oracle_attn_multi(
+            _ptr(qb), _ptr(kb), _ptr(vb), qb.dtype.itemsize, _ptr(bt), bt.shape[1], _ptr(cl), _ptr(cu), s,
+            hq, hkv, nb, b, d, ctypes.c_float(scale), _ptr(out)))
+        return out
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

@@ -244,3 +244,128 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Several new tokens per sequence (a chunk of a prefill split into chunks,
+ * page "x321.org/?p=939", section "Continuous batching is the other half of
+ * the story"; attention over the existing context during autoregressive
+ * generation, section "First understand what the KV cache is storing").
+ *
+ * Sequence i holds n = context_lens[i] tokens, the last q_len = cu_q[i + 1] -
+ * cu_q[i] of them new.  Query row j of the sequence is the token at position
+ * p = n - q_len + j and attends to tokens 0 .. p of the sequence (the ones it
+ * would have seen had they been generated one at a time):
+ *   out[cu_q[i] + j][h] = sum_{t <= p} w_t V[t] / sum_{t <= p} w_t,
+ *   w_t = exp(s_t - max_{u <= p} s_u),  s_t = scale * q[cu_q[i] + j][h] . K[t].
+ *
+ * q, out: [total_q][num_q_heads][head_dim] with total_q = cu_q[num_seqs];
+ * other arguments as oracle_attn_decode.  ORACLE_ERR_LEN if q_len > n or
+ * q_len < 0.
+ */
+static int attend_causal(const void *q, const void *k_cache, const void *v_cache, int elem_bytes,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq, int64_t n,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t num_blocks,
+                         int32_t block_size, int32_t head_dim, double scale, int32_t i,
+                         int64_t qrow, int64_t pos, int32_t h, double *out_row)
+{
+    const int64_t D = head_dim;
+    const int32_t g = h / (num_q_heads / num_kv_heads);
+    const int64_t visible = pos + 1;
+    double *s, *qv;
+    double m, denom;
+    int64_t t, x;
+
+    for (x = 0; x < D; ++x)
+        out_row[x] = 0.0;
+    if (n > (int64_t)max_blocks_per_seq * block_size)
+        return ORACLE_ERR_LEN;
+    s = (double *)malloc(sizeof(double) * (size_t)visible);
+    qv = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!s || !qv) {
+        free(s); free(qv);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (x = 0; x < D; ++x)
+        qv[x] = load_elem(q, (qrow * num_q_heads + h) * D + x, elem_bytes);
+    /* scores of the visible tokens, each key read through the block table */
+    for (t = 0; t < visible; ++t) {
+        int64_t phys = block_tables[(int64_t)i * max_blocks_per_seq + t / block_size];
+        int64_t base;
+        double acc = 0.0;
+        if (phys < 0 || phys >= num_blocks) {
+            free(s); free(qv);
+            return ORACLE_ERR_TABLE;
+        }
+        base = ((phys * num_kv_heads + g) * block_size + t % block_size) * D;
+        for (x = 0; x < D; ++x)
+            acc += qv[x] * load_elem(k_cache, base + x, elem_bytes);
+        s[t] = scale * acc;
+    }
+    m = s[0];
+    for (t = 1; t < visible; ++t)
+        if (s[t] > m)
+            m = s[t];
+    denom = 0.0;
+    for (t = 0; t < visible; ++t) {
+        s[t] = exp(s[t] - m);
+        denom += s[t];
+    }
+    for (t = 0; t < visible; ++t) {
+        int64_t phys = block_tables[(int64_t)i * max_blocks_per_seq + t / block_size];
+        int64_t base = ((phys * num_kv_heads + g) * block_size + t % block_size) * D;
+        for (x = 0; x < D; ++x)
+            out_row[x] += s[t] * load_elem(v_cache, base + x, elem_bytes);
+    }
+    for (x = 0; x < D; ++x)
+        out_row[x] /= denom;
+    free(s); free(qv);
+    return ORACLE_OK;
+}
+
+int oracle_attn_multi(const void *q, const void *k_cache, const void *v_cache, int32_t elem_bytes,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, const int32_t *cu_q, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t num_blocks,
+                      int32_t block_size, int32_t head_dim, float scale, double *out)
+{
+    int64_t total, r;
+    int32_t i;
+    int32_t *row_seq;
+    int err = ORACLE_OK;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || block_size <= 0 ||
+        head_dim <= 0 || max_blocks_per_seq <= 0 || (elem_bytes != 2 && elem_bytes != 4) ||
+        cu_q[0] != 0)
+        return ORACLE_ERR_ARGS;
+    for (i = 0; i < num_seqs; ++i) {
+        const int32_t ql = cu_q[i + 1] - cu_q[i];
+        if (ql < 0 || ql > context_lens[i])
+            return ORACLE_ERR_LEN;
+    }
+    total = cu_q[num_seqs];
+    row_seq = (int32_t *)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));
+    if (!row_seq)
+        return ORACLE_ERR_NOMEM;
+    for (i = 0; i < num_seqs; ++i)
+        for (r = cu_q[i]; r < cu_q[i + 1]; ++r)
+            row_seq[r] = i;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < total * num_q_heads; ++r) {
+        const int64_t qrow = r / num_q_heads;
+        const int32_t h = (int32_t)(r % num_q_heads);
+        const int32_t s = row_seq[qrow];
+        const int64_t n = context_lens[s];
+        const int64_t ql = cu_q[s + 1] - cu_q[s];
+        const int64_t pos = n - ql + (qrow - cu_q[s]);
+        int e = attend_causal(q, k_cache, v_cache, elem_bytes, block_tables, max_blocks_per_seq, n,
+                              num_q_heads, num_kv_heads, num_blocks, block_size, head_dim,
+                              (double)scale, s, qrow, pos, h, out + r * head_dim);
+        if (e != ORACLE_OK) {
+#pragma omp critical
+            err = e;
+        }
+    }
+    free(row_seq);
+    return err;
+}

@@ -383,9 +383,83 @@ def pin_errors(o) -> None:
         raise AssertionError("oracle accepted a slot outside the pool")
 
 
+# --------------------------------------------------------------------------
+# Several new tokens per sequence (causal)
+# --------------------------------------------------------------------------
+
+def _multi_case(seed: int, lengths: List[int], q_lens: List[int], hq: int, hkv: int, d: int, b: int):
+    rng = np.random.default_rng(seed)
+    case = Case(rng, lengths, hq, hkv, d, b)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    qm = rng.standard_normal((int(cu[-1]), hq, d)).astype(np.float32)
+    return case, cu, qm
+
+
+def sdpa_causal(q_rows: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """SDPA in fp64 for the last len(q_rows) tokens of a contiguous sequence, each seeing itself and
+    every earlier token (an explicit boolean mask; torch's own is_causal aligns the other corner)."""
+    ql, hq, d = q_rows.shape
+    n, hkv, _ = K.shape
+    g = hq // hkv
+    qt = torch.from_numpy(q_rows.astype(np.float64)).permute(1, 0, 2)                 # [hq][ql][d]
+    kt = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, dim=0)
+    vt = torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, dim=0)
+    pos = torch.arange(n - ql, n)[:, None]
+    mask = torch.arange(n)[None, :] <= pos                                                # [ql][n]
+    out = F.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(), attn_mask=mask, scale=float(scale))
+    return out.permute(1, 0, 2).numpy()                                                   # [ql][hq][d]
+
+
+def pin_multi_one_token_is_decode(o) -> None:
+    """One new token per sequence: the causal multi-token attention is plain decode attention."""
+    case, cu, _ = _multi_case(30, [1, 5, 16, 17, 40], [1, 1, 1, 1, 1], 4, 2, 16, 4)
+    got = o.attn_multi(case.q, case.pool_k, case.pool_v, case.tables, case.ctx, cu, case.scale)
+    ref = case.run(o)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def pin_multi_sdpa_causal(o) -> None:
+    """Against fp64 SDPA with an explicit causal mask on the contiguous K/V, for GQA shapes and q_len up to n."""
+    for seed, lengths, q_lens, hq, hkv in ((31, [7, 20, 33], [3, 1, 8], 4, 2), (32, [9, 12], [9, 5], 8, 8),
+                                           (33, [64, 3], [16, 2], 2, 1)):
+        case, cu, qm = _multi_case(seed, lengths, q_lens, hq, hkv, 16, 4)
+        got = o.attn_multi(qm, case.pool_k, case.pool_v, case.tables, case.ctx, cu, case.scale)
+        for i, (n, ql) in enumerate(zip(lengths, q_lens)):
+            ref = sdpa_causal(qm[cu[i]:cu[i + 1]], case.K[i], case.V[i], case.scale)
+            assert np.max(np.abs(got[cu[i]:cu[i + 1]] - ref)) <= 1e-12, (seed, i)
+
+
+def pin_multi_rows_are_truncated_decodes(o) -> None:
+    """Query row j of a sequence equals decode attention over the sequence cut after position n - q_len + j."""
+    case, cu, qm = _multi_case(34, [13, 26], [4, 6], 4, 1, 8, 4)
+    got = o.attn_multi(qm, case.pool_k, case.pool_v, case.tables, case.ctx, cu, case.scale)
+    for i, n in enumerate(case.lengths):
+        ql = int(cu[i + 1] - cu[i])
+        for j in range(ql):
+            ctx = np.zeros_like(case.ctx)
+            ctx[i] = n - ql + j + 1
+            q = np.zeros_like(case.q)
+            q[i] = qm[cu[i] + j]
+            ref = o.attn_decode(q, case.pool_k, case.pool_v, case.tables, ctx, case.scale)[i]
+            assert np.max(np.abs(got[cu[i] + j] - ref)) <= 1e-12, (i, j)
+
+
+def pin_multi_errors(o) -> None:
+    """More new tokens than the sequence holds is reported."""
+    case, _, qm = _multi_case(35, [3], [3], 2, 1, 8, 4)
+    try:
+        o.attn_multi(np.concatenate([qm, qm[:1]]), case.pool_k, case.pool_v, case.tables, case.ctx,
+                     np.array([0, 4], np.int32), case.scale)
+    except RuntimeError:
+        return
+    raise AssertionError("oracle accepted q_len > context length")
+
+
 ORACLE_PINS = [
     pin_block_map, pin_brute_force, pin_bf16_widening, pin_single_token, pin_flat_attention,
     pin_needle, pin_identical_queries, pin_placement_invariance, pin_shared_blocks,
     pin_empty_sequence, pin_row_sample, pin_write, pin_errors,
+    pin_multi_one_token_is_decode, pin_multi_sdpa_causal, pin_multi_rows_are_truncated_decodes,
+    pin_multi_errors,
 ]
 ARITH_PINS = [pin_block_arithmetic, pin_kv_bytes]

@@ -43,6 +43,12 @@ MUTANTS = {
     "write_skip_ignored": ("if (slot < 0)\n            continue;", "if (slot < -1)\n            continue;"),
     "write_head_fixed": ("int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes;",
                          "int64_t dst = ((blk * num_kv_heads + 0) * block_size + off) * row_bytes;"),
+    "multi_sees_next_token": ("const int64_t visible = pos + 1;", "const int64_t visible = pos + 2 < n ? pos + 2 : n;"),
+    "multi_mask_top_left": ("const int64_t pos = n - ql + (qrow - cu_q[s]);", "const int64_t pos = qrow - cu_q[s];"),
+    "multi_previous_query_row": ("qv[x] = load_elem(q, (qrow * num_q_heads + h) * D + x, elem_bytes);",
+                                 "qv[x] = load_elem(q, ((qrow > 0 ? qrow - 1 : 0) * num_q_heads + h) * D + x, elem_bytes);"),
+    "multi_value_is_key": ("out_row[x] += s[t] * load_elem(v_cache, base + x, elem_bytes);",
+                           "out_row[x] += s[t] * load_elem(k_cache, base + x, elem_bytes);"),
 }
 
 CHILD = r"""
