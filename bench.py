@@ -44,7 +44,9 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", default="hc_b256",
-                   choices=["tiny", "llama8b_b64", "hc_b256", "long32k", "shared_prefix"])
+                   choices=["tiny", "llama8b_b64", "hc_b256", "long32k", "shared_prefix",
+                            "multi_spec4", "multi_chunk64"],
+                   help="multi_* are steps with several new tokens per sequence (paged_attn_decode_multi)")
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 fast")
     p.add_argument("--grid-waves", type=int, default=0, help="fast kernel: waves sharing the work (0 = library choice)")
@@ -204,10 +206,103 @@ def ingest_counters(args) -> int:
     return 0
 
 
+def bench_multi(args) -> int:
+    """A step with several new tokens per sequence: paged_kv_write of the new tokens, then the causal
+    multi-token attention.  value = new tokens per second; the roofline prices the attention call on the
+    KV bytes read once per (sequence, KV head) plus q and out, and reports its matrix-core rate."""
+    import paged_kv_cache_276_amd as pkv
+    from workloads import make_multi_config
+
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    w = make_multi_config(args.config)
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, kn, vn = w.q.to(dev), w.k_new.to(dev), w.v_new.to(dev)
+    sm = torch.from_numpy(w.slot_mapping).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    cu = torch.from_numpy(w.cu_q).to(dev)
+    TQ = int(w.cu_q[-1])
+    mq = int(np.max(np.diff(w.cu_q)))
+    plan = pkv.paged_attn_multi_plan(w.num_seqs, TQ, mq, w.num_q_heads, w.max_blocks_per_seq, kc,
+                                     chunk_tokens=args.partition_tokens)
+    out = torch.empty((TQ, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty((plan["workspace_bytes"] + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+
+    def write():
+        pkv.paged_kv_write(kn, vn, sm, kc, vc)
+
+    def attend():
+        pkv.paged_attn_decode_multi(q, kc, vc, bt, cl, cu, mq, w.scale, out=out, workspace=ws,
+                                    chunk_tokens=args.partition_tokens)
+
+    for _ in range(args.warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        write()
+        ev[i][1].record()
+        attend()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    att = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) * 1e-3
+    ctx = w.context_lens.astype(np.int64)
+    ql = np.diff(w.cu_q).astype(np.int64)
+    kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
+    qo = TQ * w.num_q_heads * w.head_dim * (w.elem_bytes + 4)
+    # q.K and P.V over the visible tokens of every (new token, query head): 4 * head_dim flops per pair
+    visible = int(sum(int(ql[i]) * int(ctx[i]) - int(ql[i]) * (int(ql[i]) - 1) // 2 for i in range(w.num_seqs)))
+    flops = 4 * w.head_dim * visible * w.num_q_heads
+    rec = {
+        "metric": "multi-token attention new tokens/s (several new tokens per sequence, causal), 1 MI355X",
+        "value": TQ / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.config, "num_seqs": w.num_seqs, "new_tokens": TQ, "max_q_len": mq,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "context_tokens": int(ctx.sum()),
+                   "lengths": w.meta.get("lengths"), "chunk_tokens": plan["chunk_tokens"]},
+        "roofline": {"kernel": "paged_attn_decode_multi (chunk + merge kernels, one call)", "bound": "hbm",
+                     "achieved": (kv + qo) / att / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": (kv + qo) / att / 1e9 / PEAK_HBM_GBS, "traffic": None},
+        "attention_us": att * 1e6,
+        "mfma_TFLOPs": flops / att / 1e12,
+        "mfma_frac_of_bf16_peak": flops / att / 2.5e15,
+        "write_us": statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) * 1e3,
+    }
+    if not args.no_parity:
+        import oracle
+
+        fresh = make_multi_config(args.config)
+        o = oracle.Oracle()
+        rk, rv = oracle._bits(fresh.k_cache).copy(), oracle._bits(fresh.v_cache).copy()
+        o.kv_write(fresh.k_new, fresh.v_new, fresh.slot_mapping, rk, rv, fresh.block_size)
+        ref = o.attn_multi(fresh.q, rk, rv, fresh.block_tables, fresh.context_lens, fresh.cu_q, fresh.scale)
+        g = out.double().cpu().numpy()
+        rec["parity"] = {"max_err_over_allowed": float(np.max(np.abs(g - ref) / (2e-3 + 1e-2 * np.abs(ref)))),
+                         "finite": bool(np.isfinite(g).all())}
+    rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.ingest_counters:
         return ingest_counters(args)
+    if args.config.startswith("multi_"):
+        if args.gpus != 1:
+            print(json.dumps({"error": "this benchmark runs on exactly one GPU"}))
+            return 2
+        return bench_multi(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "the multi-GPU path is a design note, not a measured configuration"}))

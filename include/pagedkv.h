@@ -237,6 +237,54 @@ pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const vo
                                     const pkv_cache_desc *cache, const pkv_decode_opts *opts,
                                     void *stream);
 
+/*
+ * paged_attn_multi_plan -- host-only plan of paged_attn_decode_multi:
+ * partition_tokens = tokens per context chunk, max_partitions = chunks of the
+ * longest table, grid_blocks = workgroups of the chunk kernel,
+ * workspace_bytes.  Shapes as PKV_KERNEL_FAST; max_q_len * (num_q_heads /
+ * num_kv_heads) / 64 row blocks per KV head, at most 65535 in all.
+ * opts->partition_tokens, if nonzero, sets the chunk (a multiple of 16, at
+ * most 1024).
+ */
+pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, const pkv_cache_desc *cache,
+                                 const pkv_decode_opts *opts, pkv_decode_plan *plan);
+
+/*
+ * paged_attn_decode_multi -- attention from several new tokens per sequence
+ * over the paged cache, each token seeing the tokens up to its own position:
+ * the step of a prefill split into chunks, or the verification of several
+ * drafted tokens (page "x321.org/?p=939", section "Continuous batching is the
+ * other half of the story"; attention over the existing context, section
+ * "First understand what the KV cache is storing").  Sequence i's new tokens
+ * are the last q_len = cu_q_lens[i + 1] - cu_q_lens[i] of its
+ * context_lens[i] tokens (already written with paged_kv_write); new token j
+ * is at position context_lens[i] - q_len + j and
+ *   out[cu_q_lens[i] + j][h] = softmax over tokens 0 .. that position of
+ *                              scale * q[cu_q_lens[i] + j][h] . K  times V.
+ * Each context tile is read once per (sequence, KV head) for all of its new
+ * tokens; the q . K and P . V products run on the matrix cores.
+ *
+ *   q            (device) [total_q][num_q_heads][head_dim] bf16
+ *   cu_q_lens    (device) int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing,
+ *                cu_q_lens[num_seqs] = total_q
+ *   max_q_len    (host) at least every q_len; sizes the grid
+ *   out          (device) fp32 [total_q][num_q_heads][head_dim]
+ * Everything else as paged_attn_decode; the workspace is
+ * paged_attn_multi_plan's (no initialisation needed).
+ *
+ * Device contents are not validated on the host.  A sequence with q_len < 1,
+ * q_len > max_q_len or > context_lens[i], or a length past the table, gets NaN
+ * rows (for its first max_q_len tokens); offsets outside [0, total_q] leave
+ * that sequence's rows unwritten.  The kernels stay inside their buffers.
+ */
+pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *cu_q_lens, int32_t num_seqs,
+                                   int32_t total_q, int32_t max_q_len, int32_t num_q_heads, float scale,
+                                   float *out, void *workspace, uint64_t workspace_bytes,
+                                   const pkv_cache_desc *cache, const pkv_decode_opts *opts, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *pkv_status_string(pkv_status status);
 

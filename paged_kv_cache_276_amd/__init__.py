@@ -10,6 +10,8 @@ CPU or PyTorch fallback.
     out = paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale)
     out = paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens,
                                    seq_prefix_tokens, groups, max_prefix_tokens, scale)
+    out = paged_attn_decode_multi(q, k_cache, v_cache, block_tables, context_lens,
+                                  cu_q_lens, max_q_len, scale)       # several new tokens each
     paged_block_copy(k_cache, v_cache, pairs)      # copy-on-write of whole blocks
     BlockManager(num_blocks, block_size)           # host block manager (blocks.py)
 
@@ -44,7 +46,9 @@ __all__ = [
     "paged_block_copy",
     "paged_kv_write",
     "paged_attn_decode",
+    "paged_attn_decode_multi",
     "paged_attn_decode_prefix",
+    "paged_attn_multi_plan",
     "paged_attn_prefix_plan",
     "paged_attn_plan",
     "paged_attn_workspace_bytes",
@@ -277,4 +281,61 @@ def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), ctypes.byref(desc),
         ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)), s)
     _lib.check(st, "paged_attn_decode_prefix")
+    return out
+
+
+def paged_attn_multi_plan(num_seqs: int, total_q: int, max_q_len: int, num_q_heads: int, max_blocks_per_seq: int,
+                          cache, chunk_tokens: int = 0) -> Dict[str, int]:
+    """Host-only plan of the multi-token attention (context chunk, chunks, workgroups, workspace bytes)."""
+    desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
+    plan = DecodePlan()
+    st = _lib.lib().paged_attn_multi_plan(num_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq,
+                                          ctypes.byref(desc), ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, 0)),
+                                          ctypes.byref(plan))
+    _lib.check(st, "paged_attn_multi_plan")
+    return {"chunk_tokens": plan.partition_tokens, "max_chunks": plan.max_partitions,
+            "workgroups": plan.grid_blocks, "workspace_bytes": plan.workspace_bytes}
+
+
+def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, cu_q_lens: torch.Tensor,
+                            max_q_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, chunk_tokens: int = 0,
+                            stream=None) -> torch.Tensor:
+    """Causal attention of several new tokens per sequence over the paged cache (fp32 out [total_q][Hq][D])."""
+    dev = k_cache.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (cu_q_lens, "cu_q_lens")):
+        _dev(t, n, dev)
+    desc = cache_desc(k_cache)
+    _need(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache/v_cache differ")
+    _need(q.dim() == 3 and q.shape[2] == desc.head_dim and q.dtype == k_cache.dtype,
+          "q must be [total_q][Hq][D] of the cache dtype")
+    TQ, Hq = q.shape[0], q.shape[1]
+    S = context_lens.shape[0]
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S,
+          "block_tables must be int32 [S][max_blocks_per_seq]")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1, "context_lens must be int32 [S]")
+    _need(cu_q_lens.dtype == torch.int32 and tuple(cu_q_lens.shape) == (S + 1,), "cu_q_lens must be int32 [S+1]")
+    if out is None:
+        out = torch.empty((TQ, Hq, desc.head_dim), dtype=torch.float32, device=dev)
+    _dev(out, "out", dev)
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (TQ, Hq, desc.head_dim), "out must be fp32 [total_q][Hq][D]")
+    maxb = block_tables.shape[1]
+    plan = paged_attn_multi_plan(S, TQ, max_q_len, Hq, maxb, desc, chunk_tokens)
+    s = _stream(dev, stream)
+    need = plan["workspace_bytes"]
+    if workspace is None:
+        workspace = _workspace(dev, int(s.value or 0), need)
+    else:
+        _dev(workspace, "workspace", dev)
+        _need(workspace.numel() * workspace.element_size() >= need, f"workspace needs {need} bytes")
+    st = _lib.lib().paged_attn_decode_multi(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), maxb, ctypes.c_void_p(context_lens.data_ptr()),
+        ctypes.c_void_p(cu_q_lens.data_ptr()), S, TQ, int(max_q_len), Hq, ctypes.c_float(scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), ctypes.byref(desc),
+        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, 0)), s)
+    _lib.check(st, "paged_attn_decode_multi")
     return out

@@ -27,6 +27,8 @@ EXPORTS = (
     "paged_attn_decode",
     "paged_attn_prefix_plan",
     "paged_attn_decode_prefix",
+    "paged_attn_multi_plan",
+    "paged_attn_decode_multi",
     "paged_block_copy",
     "pkv_status_string",
     "pkv_version",
@@ -104,6 +106,11 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode_prefix.restype = ctypes.c_int
     L.paged_attn_decode_prefix.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, i32, i32, ctypes.c_float,
                                            vp, vp, u64, P(CacheDesc), P(DecodeOpts), vp]
+    L.paged_attn_multi_plan.restype = ctypes.c_int
+    L.paged_attn_multi_plan.argtypes = [i32, i32, i32, i32, i32, P(CacheDesc), P(DecodeOpts), P(DecodePlan)]
+    L.paged_attn_decode_multi.restype = ctypes.c_int
+    L.paged_attn_decode_multi.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                                          vp, vp, u64, P(CacheDesc), P(DecodeOpts), vp]
     L.paged_block_copy.restype = ctypes.c_int
     L.paged_block_copy.argtypes = [vp, vp, vp, i32, P(CacheDesc), vp]
     i64 = ctypes.c_int64

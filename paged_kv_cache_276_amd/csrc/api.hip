@@ -354,6 +354,111 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+namespace {
+
+// Several new tokens per sequence: chunks of the context per (sequence, KV
+// head, 64-row block) and the chunk partials.
+struct MultiPlan {
+    pkv_decode_plan base;
+    int32_t chunk_tiles, max_chunks, row_blocks;
+    uint64_t pml_bytes, pacc_bytes, total;
+};
+
+pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq, const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                           MultiPlan* mp) {
+    pkv_decode_opts o = opts ? *opts : pkv_decode_opts{0, PKV_KERNEL_AUTO, 0};
+    const int32_t chunk_tokens = o.partition_tokens;
+    o.partition_tokens = 0;
+    o.kernel = PKV_KERNEL_FAST;
+    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &mp->base);
+    if (st != PKV_OK) return st;
+    if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
+    if (total_q < 0 || max_q_len < 1) return PKV_ERR_SHAPE;
+    const int32_t group = num_q_heads / cache->num_kv_heads;
+    const int64_t rb = ((int64_t)max_q_len * group + 63) / 64;
+    if (rb * cache->num_kv_heads > 65535 || (int64_t)max_q_len > 65535 || num_seqs > INT32_MAX - 1) return PKV_ERR_SHAPE;
+    const int64_t tiles = ((int64_t)max_blocks_per_seq * cache->block_size + 15) / 16;
+    int64_t ct;
+    if (chunk_tokens) {
+        if (chunk_tokens < 0 || chunk_tokens % 16 != 0 || chunk_tokens / 16 > kPrefixChunkTilesMax) return PKV_ERR_SHAPE;
+        ct = chunk_tokens / 16;
+    } else {
+        ct = (tiles * num_seqs * cache->num_kv_heads * rb + kPrefixTargetWorkgroups - 1) / kPrefixTargetWorkgroups;
+        ct = ct < 8 ? 8 : (ct > kPrefixChunkTilesMax ? kPrefixChunkTilesMax : ct);
+    }
+    const int64_t mc = (tiles + ct - 1) / ct;
+    if (mc > 65535) return PKV_ERR_SHAPE;
+    mp->chunk_tiles = (int32_t)ct;
+    mp->max_chunks = (int32_t)mc;
+    mp->row_blocks = (int32_t)rb;
+    const uint64_t rows = (uint64_t)total_q * num_q_heads * (uint64_t)mc;
+    mp->pml_bytes = align_up(rows * sizeof(float2), 256);
+    mp->pacc_bytes = rows * (uint64_t)cache->head_dim * sizeof(float);
+    mp->total = mp->pml_bytes + mp->pacc_bytes;
+    mp->base.partition_tokens = (int32_t)ct * 16;
+    mp->base.max_partitions = mp->max_chunks;
+    mp->base.grid_blocks = (int64_t)num_seqs * cache->num_kv_heads * rb * mc;
+    mp->base.threads_per_block = 256;
+    mp->base.workspace_bytes = mp->total;
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_API pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                                         int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                         const pkv_decode_opts* opts, pkv_decode_plan* plan) {
+    if (!plan) return PKV_ERR_NULL;
+    MultiPlan mp;
+    const pkv_status st = make_multi_plan(num_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, cache, opts, &mp);
+    if (st == PKV_OK) *plan = mp.base;
+    return st;
+}
+
+PKV_API pkv_status paged_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, const int32_t* cu_q_lens, int32_t num_seqs,
+                                           int32_t total_q, int32_t max_q_len, int32_t num_q_heads, float scale,
+                                           float* out, void* workspace, uint64_t workspace_bytes,
+                                           const pkv_cache_desc* cache, const pkv_decode_opts* opts, void* stream) {
+    MultiPlan mp;
+    pkv_status st = make_multi_plan(num_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, cache, opts, &mp);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0 || total_q == 0) return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens || !out) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_ERR_ALIGN;
+    if (!workspace || workspace_bytes < mp.total) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    char* ws = static_cast<char*>(workspace);
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.num_blocks = cache->num_blocks;
+    a.block_size = cache->block_size;
+    a.head_dim = cache->head_dim;
+    a.dtype = cache->dtype;
+    a.scale = scale;
+    a.out = out;
+    a.cu_q = cu_q_lens;
+    a.total_q = total_q;
+    a.max_q_len = max_q_len;
+    a.multi_row_blocks = mp.row_blocks;
+    a.prefix_chunk_tiles = mp.chunk_tiles;
+    a.prefix_max_chunks = mp.max_chunks;
+    a.ws_pml = reinterpret_cast<float2*>(ws);
+    a.ws_pacc = reinterpret_cast<float*>(ws + mp.pml_bytes);
+    const hipError_t e = pkv::launch_decode_multi(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 PKV_API const char* pkv_status_string(pkv_status status) {
     switch (status) {
         case PKV_OK: return "ok";

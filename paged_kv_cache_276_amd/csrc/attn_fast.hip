@@ -891,6 +891,254 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
     }
 }
 
+// Several new tokens per sequence, causal.  Workgroup (sequence i, KV head g
+// and block of 64 query rows, chunk c of the sequence's tiles) has four waves
+// and the tile pipeline of decode_prefix_kernel: each 16-token tile of the
+// chunk is read once into LDS for all of the sequence's new tokens.  Row r of
+// a block is new token r / G (position ctx - q_len + r / G) and head r % G; a
+// row sees the tokens up to its own position (the others are masked in the
+// scores).  Each row leaves the chunk's (m, l, acc) for multi_merge_kernel.
+template <int BS, int G>
+__global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const DecodeArgs a, float qscale) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid / kWave;
+    const int i = blockIdx.x;
+    const int rbs = a.multi_row_blocks;
+    const int g = blockIdx.y / rbs, rb = blockIdx.y % rbs;
+    const int c = blockIdx.z;
+    const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int maxB = a.max_blocks_per_seq;
+    const int table_tokens = maxB * BS;
+    const int CT = a.prefix_chunk_tiles;
+
+    const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
+    const int ql = q1 - q0;
+    const int ctx = a.context_lens[i];
+    // Sequences the merge reports as NaN, and blocks with no rows or tiles (uniform).
+    if (q0 < 0 || q1 > a.total_q || ql < 1 || ql > a.max_q_len || ctx < ql || ctx > table_tokens) return;
+    const int rows = ql * G;
+    if (64 * rb >= rows) return;
+    const int nt_total = (ctx + kTok - 1) / kTok;
+    const int t0 = c * CT;
+    const int t1 = min(t0 + CT, nt_total);
+    const int ntile = t1 - t0;
+    if (ntile <= 0) return;
+    const bool computes = 64 * rb + 16 * wv < rows;
+
+    __shared__ uint2 toff_lds[kPrefixChunkTilesMax];
+    __shared__ int tbad_lds[kPrefixChunkTilesMax];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
+    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][kHd * kVtRow];
+
+    const int32_t* __restrict__ bt = a.block_tables;
+    if (tid < ntile) {
+        const int tok0 = (t0 + tid) * kTok;
+        const int phys = bt[(int64_t)i * maxB + tok0 / BS];
+        const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
+        const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * kHd;
+        toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
+        tbad_lds[tid] = badp;
+    }
+    // This lane's row (for the scores and the softmax state): new token jq, head hq.
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const int row = 64 * rb + 16 * wv + r16;
+    const bool real = row < rows;
+    const int jq = real ? row / G : 0;
+    const int pos = ctx - ql + jq;  // last token this row sees
+    uint4 qc[4];
+    {
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? row % G : 0)) * kHd;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
+            qc[kq] = real ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
+    const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
+    const int vtg = tid >> 6, vj = tid & 63;
+    struct TileKV {
+        uint4 k, v;
+    };
+    auto load_tile = [&](int j) -> TileKV {
+        const uint2 o = toff_lds[j];
+        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)(4 * vtg) * (kHd / 2) + vj;
+        TileKV t;
+        t.k = make_uint4(k32[off], k32[off + kHd / 2], k32[off + 2 * (kHd / 2)], k32[off + 3 * (kHd / 2)]);
+        t.v = make_uint4(v32[off], v32[off + kHd / 2], v32[off + 2 * (kHd / 2)], v32[off + 3 * (kHd / 2)]);
+        return t;
+    };
+    // Value rows past the end of the context (the tail of the last tile) are
+    // stored as zeros: their weights are zero, and 0 * (whatever the slot
+    // holds, NaN included) must not reach the sums.  Key rows there only give
+    // scores that the mask replaces.
+    auto store_tile = [&](int buf, const TileKV& t, int j) {
+        unsigned char* kb = &k_lds[buf][(4 * vtg) * kKRow + 4 * vj];
+        *reinterpret_cast<uint32_t*>(kb) = t.k.x;
+        *reinterpret_cast<uint32_t*>(kb + kKRow) = t.k.y;
+        *reinterpret_cast<uint32_t*>(kb + 2 * kKRow) = t.k.z;
+        *reinterpret_cast<uint32_t*>(kb + 3 * kKRow) = t.k.w;
+        const int tokb = (t0 + j) * kTok + 4 * vtg;
+        uint4 v = t.v;
+        v.x = tokb < ctx ? v.x : 0u;
+        v.y = tokb + 1 < ctx ? v.y : 0u;
+        v.z = tokb + 2 < ctx ? v.z : 0u;
+        v.w = tokb + 3 < ctx ? v.w : 0u;
+        const uint2 even = make_uint2((v.x & 0xffffu) | (v.y << 16), (v.z & 0xffffu) | (v.w << 16));
+        const uint2 odd = make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj) * kVtRow + 8 * vtg]) = even;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj + 1) * kVtRow + 8 * vtg]) = odd;
+    };
+
+    f32x4 acc[kHd / 16];
+#pragma unroll
+    for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    float l = 0.f;
+    bool bad = false;
+
+    auto step = [&](int buf, int j) {
+        bad = bad || tbad_lds[j] != 0;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qc[kq]), sc, 0, 0, 0);
+        }
+        const int tok = (t0 + j) * kTok + 4 * grp;
+        float s[4];
+        bool vis[4];
+        bool need = false;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vis[r] = real && tok + r <= pos;
+            s[r] = vis[r] ? sc[r] * qscale : -INFINITY;
+            need = need || (vis[r] && s[r] > m + kLazyRescale);
+        }
+        if (__any(need)) {
+            float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+            const float mn = tm > m + kLazyRescale ? tm : m;
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+                for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
+            }
+        }
+        s16x4 phi, plo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = vis[r] ? fast_exp2(s[r] - m) : 0.f;
+            l += pr;
+            const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
+            phi[r] = (short)(hb >> 16);
+            plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
+        }
+#pragma unroll
+        for (int jb = 0; jb < kHd / 16; ++jb) {
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * jb + r16) * kVtRow + 8 * grp]);
+            const s16x4 vv = __builtin_bit_cast(s16x4, vb);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
+        }
+    };
+
+    TileKV R[kPrefixAhead];
+#pragma unroll
+    for (int q = 0; q < kPrefixAhead; ++q) R[q] = load_tile(min(q, ntile - 1));
+    int j0 = 0;
+    for (; j0 + kPrefixAhead <= ntile; j0 += kPrefixAhead) {
+#pragma unroll
+        for (int q = 0; q < kPrefixAhead; ++q) {
+            const int j = j0 + q;
+            store_tile(j & 1, R[q], j);
+            R[q] = load_tile(min(j + kPrefixAhead, ntile - 1));
+            __syncthreads();
+            if (computes) step(j & 1, j);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kPrefixAhead - 1; ++q) {
+        const int j = j0 + q;
+        if (j < ntile) {  // uniform
+            store_tile(j & 1, R[q], j);
+            __syncthreads();
+            if (computes) step(j & 1, j);
+        }
+    }
+
+    if (!computes) return;
+    float lt = l + __shfl_xor(l, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int MC = a.prefix_max_chunks;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        const int r = 64 * rb + 16 * wv + 4 * grp + rr;
+        if (r < rows) {
+            const int64_t pr = ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + c;
+#pragma unroll
+            for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[jb][rr];
+        }
+    }
+    if (lane < 16 && real) {
+        const int64_t pr = ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + row % G) * MC + c;
+        a.ws_pml[pr] = make_float2(m, bad ? NAN : lt);
+    }
+}
+
+// Merge of the chunk partials of one new token's G heads (wave h = head g*G+h,
+// lanes own two columns): out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c
+// over the sequence's chunks in order (chunks past a token's position carry
+// m = -inf and weigh nothing).  Invalid sequence descriptions give NaN rows.
+template <int G>
+__global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a, int table_tokens) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int h = threadIdx.x / kWave;
+    const int i = blockIdx.x, j = blockIdx.y, g = blockIdx.z;
+    const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
+    const int ql = q1 - q0;
+    if (q0 < 0 || q1 > a.total_q || ql < 1 || j >= ql) return;  // no row to write
+    const int ctx = a.context_lens[i];
+    const int64_t orow = (int64_t)(q0 + j) * a.num_q_heads + (int64_t)g * G + h;
+    float2* out = reinterpret_cast<float2*>(a.out + orow * kHd + 2 * lane);
+    const int CT = a.prefix_chunk_tiles;
+    const int nch = ctx >= 1 ? ((ctx + kTok - 1) / kTok + CT - 1) / CT : 0;
+    if (ql > a.max_q_len || ctx < ql || ctx > table_tokens || nch > a.prefix_max_chunks) {
+        *out = make_float2(NAN, NAN);
+        return;
+    }
+    const int64_t base = orow * a.prefix_max_chunks;
+    float M = -INFINITY;
+    for (int p = lane; p < nch; p += kWave) M = fmaxf(M, a.ws_pml[base + p].x);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int p = lane; p < nch; p += kWave) {
+        const float2 v = a.ws_pml[base + p];
+        L += v.x == -INFINITY ? 0.f : exp2f(v.x - M) * v.y;
+    }
+    L = wave_sum(L);
+    float o0 = 0.f, o1 = 0.f;
+    for (int p = 0; p < nch; ++p) {
+        const float mp = a.ws_pml[base + p].x;
+        if (mp == -INFINITY) continue;  // uniform
+        const float wgt = exp2f(mp - M);
+        const float2 v = *reinterpret_cast<const float2*>(a.ws_pacc + (base + p) * kHd + 2 * lane);
+        o0 = fmaf(wgt, v.x, o0);
+        o1 = fmaf(wgt, v.y, o1);
+    }
+    *out = make_float2(o0 / L, o1 / L);
+}
+
 namespace {
 
 // Resident waves of one kernel on the current device (cached).
@@ -921,6 +1169,28 @@ hipError_t launch_prefix_chunks(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_prefix_kernel<BS, G>), grid, dim3(kPrefixThreads), 0, stream, a,
                        a.scale * kLog2e);
     return hipGetLastError();
+}
+
+template <int BS, int G>
+hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.num_seqs, (unsigned)(a.num_kv_heads * a.multi_row_blocks), (unsigned)a.prefix_max_chunks);
+    hipLaunchKernelGGL((multi_query_kernel<BS, G>), grid, dim3(kPrefixThreads), 0, stream, a, a.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid((unsigned)a.num_seqs, (unsigned)a.max_q_len, (unsigned)a.num_kv_heads);
+    hipLaunchKernelGGL((multi_merge_kernel<G>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
+    return hipGetLastError();
+}
+
+template <int BS>
+hipError_t multi_by_group(const DecodeArgs& a, hipStream_t stream) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_multi_t<BS, 1>(a, stream);
+        case 2: return launch_multi_t<BS, 2>(a, stream);
+        case 4: return launch_multi_t<BS, 4>(a, stream);
+        case 8: return launch_multi_t<BS, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int BS, int G, bool PREFIX>
@@ -966,6 +1236,16 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
         case 16: return by_group<16, false>(a, stream);
         case 32: return by_group<32, false>(a, stream);
         case 64: return by_group<64, false>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
+    if (a.num_seqs == 0 || a.total_q == 0) return hipSuccess;
+    switch (a.block_size) {
+        case 16: return multi_by_group<16>(a, stream);
+        case 32: return multi_by_group<32>(a, stream);
+        case 64: return multi_by_group<64>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -39,6 +39,12 @@ struct DecodeArgs {
     int32_t prefix_max_chunks;   // chunk partials kept per (sequence, KV head)
     float2* ws_pml;              // prefix partials (m, l): [S][Hkv][max_chunks][G]
     float* ws_pacc;              // prefix partials acc: [S][Hkv][max_chunks][G][head_dim]
+    // Several new tokens per sequence (paged_attn_decode_multi); chunk partials
+    // go to ws_pml / ws_pacc as [total_q][Hq][max_chunks] (m, l) and acc.
+    const int32_t* cu_q;         // [S + 1] offsets of each sequence's query rows
+    int32_t total_q;
+    int32_t max_q_len;
+    int32_t multi_row_blocks;    // 64-row blocks per KV head
 };
 
 constexpr int32_t kMaxGridWaves = 8192;  // PKV_MAX_GRID_WAVES
@@ -56,6 +62,8 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
 // Shared-prefix decode: prefix kernel, suffix tiles (fast kernel), merge.
 hipError_t launch_decode_prefix(const DecodeArgs& a, hipStream_t stream);
+// Several new tokens per sequence (causal): chunk kernel, merge.
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);
 constexpr int32_t kPrefixGroupMax = 8;  // sequences per prefix group (one wave each)
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 

@@ -15,8 +15,12 @@ copy of that arithmetic, pinned to the pages' worked numbers.
 
 from .configs import (  # noqa: F401
     CONFIG_NAMES,
+    MULTI_CONFIG_NAMES,
+    MultiWorkload,
     Workload,
     make_config,
     make_custom,
+    make_multi,
+    make_multi_config,
     poison_value_bits,
 )

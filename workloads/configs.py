@@ -307,3 +307,81 @@ def make_custom(
         max_blocks_per_seq=max_blocks_per_seq, prefix_groups=prefix_groups,
         pool_fill=pool_fill, pool_blocks=pool_blocks, poison=poison, values=values,
     )
+
+
+@dataclass
+class MultiWorkload:
+    """Several new tokens per sequence: the cache holds ctx - q_len tokens of each
+    sequence before the step; the step writes the q_len new tokens (slots in
+    ``slot_mapping``, rows ``k_new``/``v_new`` in sequence order) and attends from
+    each of them.  ``cu_q`` [S + 1] are the offsets of each sequence's rows in
+    ``q``/``k_new``/``v_new``/``slot_mapping``."""
+
+    base: Workload
+    q_lens: np.ndarray
+    cu_q: np.ndarray
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    slot_mapping: np.ndarray
+
+    def __getattr__(self, name):  # everything else (pools, tables, shapes) comes from the base workload
+        return getattr(self.base, name)
+
+
+def make_multi(lengths: Sequence[int], q_lens: Sequence[int], num_q_heads: int = 8, num_kv_heads: int = 2,
+               head_dim: int = 128, block_size: int = 16, dtype: torch.dtype = torch.bfloat16, seed: int = 0,
+               max_blocks_per_seq: Optional[int] = None, pool_fill: float = 1.0, poison: bool = True,
+               name: str = "custom_multi", meta: Optional[Dict[str, object]] = None) -> MultiWorkload:
+    assert len(lengths) == len(q_lens) and all(0 < ql <= n for n, ql in zip(lengths, q_lens))
+    base = _build(name, seed, lengths, num_q_heads, num_kv_heads, head_dim, block_size, dtype,
+                  max_blocks_per_seq=max_blocks_per_seq, pool_fill=pool_fill, poison=False, meta=meta)
+    B = block_size
+    S = len(lengths)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    slots = np.empty(int(cu[-1]), dtype=np.int32)
+    for i, n in enumerate(lengths):
+        for j in range(int(q_lens[i])):
+            pos = int(n) - int(q_lens[i]) + j
+            slots[cu[i] + j] = int(base.block_tables[i, pos // B]) * B + pos % B
+    gen = torch.Generator().manual_seed(seed + 7919)
+    T = int(cu[-1])
+    q = torch.empty((T, num_q_heads, head_dim), dtype=dtype)
+    k_new = torch.empty((T, num_kv_heads, head_dim), dtype=dtype)
+    v_new = torch.empty((T, num_kv_heads, head_dim), dtype=dtype)
+    for t in (q, k_new, v_new):
+        _fill_normal(t, gen)
+    if poison:
+        used = set(int(p) for p in base.block_tables.reshape(-1) if p >= 0)
+        free = torch.tensor([b for b in range(base.num_blocks) if b not in used], dtype=torch.long)
+        for c in (base.k_cache, base.v_cache):
+            if free.numel():
+                tmp = c[free]
+                _poison(tmp, dtype)
+                c[free] = tmp
+            for i, n in enumerate(lengths):  # the slots the step writes, and the tail of each last block
+                first = int(n) - int(q_lens[i])
+                nblk = -(-int(n) // B)
+                for blk in range(first // B, nblk):
+                    lo = max(first - blk * B, 0)
+                    _poison(c[int(base.block_tables[i, blk]), :, lo:, :], dtype)
+    return MultiWorkload(base=base, q_lens=q_lens, cu_q=cu, q=q, k_new=k_new, v_new=v_new, slot_mapping=slots)
+
+
+MULTI_CONFIG_NAMES = ("multi_spec4", "multi_chunk64")
+
+
+def make_multi_config(name: str, poison: bool = True) -> MultiWorkload:
+    """Multi-token steps: speculative verification of 4 draft tokens on the batch-64 lengths, and
+    chunks of 64 prompt tokens appended to long contexts."""
+    if name == "multi_spec4":
+        rng = np.random.Generator(np.random.PCG64(11))
+        lengths = rng.integers(128, 4096, size=64, endpoint=True).tolist()
+        return make_multi(lengths, [4] * 64, 32, 8, 128, 16, torch.bfloat16, seed=11, max_blocks_per_seq=256,
+                          poison=poison, name=name, meta={"lengths": "uniform [128,4096]", "q_len": 4})
+    if name == "multi_chunk64":
+        lengths = [4096] * 16
+        return make_multi(lengths, [64] * 16, 32, 8, 128, 16, torch.bfloat16, seed=12, max_blocks_per_seq=256,
+                          poison=poison, name=name, meta={"lengths": "16 x 4096", "q_len": 64})
+    raise KeyError(name)
