@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="hc_b256",
                    choices=["tiny", "llama8b_b64", "hc_b256", "long32k", "shared_prefix",
                             "multi_spec4", "multi_chunk64"],
@@ -59,6 +59,9 @@ def parse_args(argv=None):
     p.add_argument("--prefix", action="store_true",
                    help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
                         "each shared block is read once per group")
+    p.add_argument("--event-stride", type=int, default=8,
+                   help="record per-launch timing events on every n-th timed step only: each event "
+                        "between two kernels leaves the stream idle for a few microseconds")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -206,6 +209,99 @@ def ingest_counters(args) -> int:
     return 0
 
 
+class _HipEvents:
+    """Timing events made with hipEventCreateWithFlags(hipEventDisableSystemFence): a timing
+    event does not need the system-scope release that torch's events ask for, which flushes
+    L2 and leaves the stream idle for microseconds around the kernels it brackets.  Falls back
+    to torch's events if the HIP runtime cannot be loaded by name."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.lib = None
+        try:
+            lib = ctypes.CDLL("libamdhip64.so")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            self.lib = lib
+        except OSError:
+            pass
+        self.kind = "hip, no system fence" if self.lib else "torch"
+
+    def new(self):
+        if not self.lib:
+            return torch.cuda.Event(enable_timing=True)
+        e = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e
+
+    def record(self, e):
+        if not self.lib:
+            e.record()
+            return
+        rc = self.lib.hipEventRecord(e, self.ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        if not self.lib:
+            return a.elapsed_time(b)
+        f = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def free(self, events):
+        if self.lib:
+            for e in events:
+                self.lib.hipEventDestroy(e)
+
+
+def timed_steps(write, decode, K: int, stride: int) -> dict:
+    """Run K steps of write() then decode() between two synchronisations.  Per-launch events
+    bracket write and decode on every stride-th step only (on the current stream, where both
+    launch); one event pair brackets the whole region for its GPU-clock length."""
+    stride = max(1, stride)
+    sampled = list(range(0, K, stride))
+    he = _HipEvents()
+    ev = {i: [he.new() for _ in range(3)] for i in sampled}
+    whole = [he.new() for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    he.record(whole[0])
+    for i in range(K):
+        e = ev.get(i)
+        if e:
+            he.record(e[0])
+        write()
+        if e:
+            he.record(e[1])
+        decode()
+        if e:
+            he.record(e[2])
+    he.record(whole[1])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    res = {
+        "ms_per_step": (t1 - t0) * 1e3 / K,
+        "gpu_ms_per_step": he.elapsed_ms(whole[0], whole[1]) / K,
+        "write_ms": [he.elapsed_ms(ev[i][0], ev[i][1]) for i in sampled],
+        "decode_ms": [he.elapsed_ms(ev[i][1], ev[i][2]) for i in sampled],
+        "event_kind": he.kind,
+        "event_stride": stride,
+    }
+    he.free([x for v in ev.values() for x in v] + whole)
+    return res
+
+
 def bench_multi(args) -> int:
     """A step with several new tokens per sequence: paged_kv_write of the new tokens, then the causal
     multi-token attention.  value = new tokens per second; the roofline prices the attention call on the
@@ -241,18 +337,9 @@ def bench_multi(args) -> int:
         attend()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        write()
-        ev[i][1].record()
-        attend()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    att = statistics.mean(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) * 1e-3
+    tm = timed_steps(write, attend, K, args.event_stride)
+    ms_per_step = tm["ms_per_step"]
+    att = statistics.mean(tm["decode_ms"]) * 1e-3
     ctx = w.context_lens.astype(np.int64)
     ql = np.diff(w.cu_q).astype(np.int64)
     kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
@@ -276,7 +363,10 @@ def bench_multi(args) -> int:
         "attention_us": att * 1e6,
         "mfma_TFLOPs": flops / att / 1e12,
         "mfma_frac_of_bf16_peak": flops / att / 2.5e15,
-        "write_us": statistics.mean(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) * 1e3,
+        "write_us": statistics.mean(tm["write_ms"]) * 1e3,
+        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "event_stride": tm["event_stride"],
+                   "events": tm["event_kind"],
+                   "sampled_launches": len(tm["decode_ms"])},
     }
     if not args.no_parity:
         import oracle
@@ -368,21 +458,11 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        write()
-        ev[i][1].record()
-        decode()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    tm = timed_steps(write, decode, K, args.event_stride)
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
-    ms_per_step = (t1 - t0) * 1e3 / K
-    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    decode_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = tm["ms_per_step"]
+    write_ms = tm["write_ms"]
+    decode_ms = tm["decode_ms"]
     dec_avg = statistics.mean(decode_ms)
     nbytes = algorithmic_bytes(w)
     # The prefix path has to move each shared block once: it is priced on the unique bytes.
@@ -443,6 +523,9 @@ def main(argv=None) -> int:
         "decode_us": dec_avg * 1e3,
         "decode_us_min": min(decode_ms) * 1e3,
         "write_us": statistics.mean(write_ms) * 1e3,
+        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "event_stride": tm["event_stride"],
+                   "events": tm["event_kind"],
+                   "sampled_launches": len(decode_ms)},
         "algorithmic_bytes": nbytes,
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,
@@ -455,14 +538,16 @@ def main(argv=None) -> int:
         scratch = torch.zeros(args.flush_mib << 18, dtype=torch.float32, device=dev)
         decode()  # evicts the zero fill's dirty lines before the first timed call
         cold = []
+        he = _HipEvents()
         for i in range(args.cold_steps):
             sink = scratch.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            e0, e1 = he.new(), he.new()
+            he.record(e0)
             decode()
-            e1.record()
+            he.record(e1)
             torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
+            cold.append(he.elapsed_ms(e0, e1) * 1e3)
+            he.free([e0, e1])
         rec["decode_us_cold"] = statistics.median(cold)
         rec["kv_read_GBps_cold"] = nbytes["kv"] / (rec["decode_us_cold"] * 1e-6) / 1e9
         del scratch, sink

@@ -113,12 +113,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     int s0 = 0;
     int total = 0;
     for (int base = 0; base < S; base += kWave * 8) {
+        // All eight loads are issued before the first is used (the index is
+        // clamped into range, the value masked after), so the pass costs one
+        // memory round trip.
+        int cv[8], sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = min(base + lane * 8 + k, S - 1);
+            cv[k] = ctxp[i];
+            sv[k] = START ? startp[i] : 0;
+        }
         int s = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = base + lane * 8 + k;
-            const int c = i < S ? ctxp[i] : 0;
-            const int st = (START && i < S) ? startp[i] : 0;
+            const int c = i < S ? cv[k] : 0;
+            const int st = (START && i < S) ? sv[k] : 0;
             const int n = tiles_at(c, st);
             if (base == 0) {
                 nv0[k] = n;
@@ -137,8 +147,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (Nt == 0) return;
     const int W = (int)(Nt < nwaves ? Nt : nwaves);
     if (w >= W) return;
-    const int64_t c0 = (int64_t)w * Nt / W;
-    const int64_t c1 = (int64_t)(w + 1) * Nt / W;
+    const int64_t c0 = div_floor((int64_t)w * Nt, W);
+    const int64_t c1 = div_floor((int64_t)(w + 1) * Nt, W);
 
     // ---- 2. the sequence holding tile c0
     int i0 = -1;
@@ -153,14 +163,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 for (int k = 0; k < 8; ++k) nv[k] = nv0[k];
                 s = s0;
             } else {
+                int cv[8], sv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int i = min(base + lane * 8 + k, S - 1);
+                    cv[k] = ctxp[i];
+                    sv[k] = START ? startp[i] : 0;
+                }
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int i = base + lane * 8 + k;
-                    nv[k] = i < S ? tiles_at(ctxp[i], START ? startp[i] : 0) : 0;
+                    nv[k] = i < S ? tiles_at(cv[k], sv[k]) : 0;
                     s += nv[k];
                 }
             }
-            const int incl = wave_incl_scan_int(s, lane);
+            const int incl = wave_incl_scan_int(s);
             const int64_t chunk = (int64_t)read_lane(incl, kWave - 1) * Hkv;
             if (c0 < acc + chunk) {
                 const unsigned long long mask = __ballot(acc + (int64_t)incl * Hkv > c0);
@@ -206,9 +223,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     P.n = tiles_at(P.ctx, P.start);
     P.seq_base = base0;
     {
-        const int64_t off = c0 - base0;
-        P.g = (int)(off / P.n);
-        P.b = (int)(off % P.n);
+        const int off = (int)(c0 - base0);  // < P.n * Hkv
+        P.g = off / P.n;
+        P.b = off - P.g * P.n;
     }
 
     const int r16 = lane & 15;  // MFMA column (token) / V column group
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         }
         if (from_start && lane == 0) {
             const int64_t last_tile = (int64_t)useq_base + (int64_t)ug * un + un - 1;
-            const int64_t w_last = ((last_tile + 1) * W - 1) / Nt;
+            const int64_t w_last = div_floor((last_tile + 1) * W - 1, Nt);
             a.ws_rec[u] = make_int2((int)slot, (int)(w_last - w + 1));
         }
     };
@@ -515,15 +532,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // tile's loads (past the end of the segment it requests its last tile
         // again, which the cache holds), so all paths issue the same loads in
         // the same order and each wait counts exactly the loads it needs.
+        // The scheduling barriers keep every tile's loads in issue order: if
+        // the compiler interleaves the loads of two tiles, the wait counts it
+        // derives at the loop head have to cover both, and the ring drains.
         if constexpr (G <= 4) {
             auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
                 if (kk < seg_len) begin(seg0 + kk, cur);
+                __builtin_amdgcn_sched_barrier(0);
                 issue(min(kk + 2, seg_len - 1), ahead);
+                __builtin_amdgcn_sched_barrier(0);
                 if (kk < seg_len) step(seg0 + kk, cur);
             };
             TileLoad X0, X1, X2;
             issue(0, X0);
+            __builtin_amdgcn_sched_barrier(0);
             issue(min(1, seg_len - 1), X1);
+            __builtin_amdgcn_sched_barrier(0);
             for (int kk = 0; kk < seg_len; kk += 3) {
                 phase(kk, X0, X2);
                 phase(kk + 1, X1, X0);
@@ -532,11 +556,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         } else {
             auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
                 if (kk < seg_len) begin(seg0 + kk, cur);
+                __builtin_amdgcn_sched_barrier(0);
                 issue(min(kk + 1, seg_len - 1), ahead);
+                __builtin_amdgcn_sched_barrier(0);
                 if (kk < seg_len) step(seg0 + kk, cur);
             };
             TileLoad X0, X1;
             issue(0, X0);
+            __builtin_amdgcn_sched_barrier(0);
             for (int kk = 0; kk < seg_len; kk += 2) {
                 phase(kk, X0, X1);
                 phase(kk + 1, X1, X0);

@@ -38,19 +38,40 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// DPP move of an int where lanes without a source, and lanes of rows outside
+// ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i0(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes, all in DPP moves (no LDS permutes):
+// a Hillis-Steele scan inside every 16-lane row (shifts by 1, 2, 4, 8), then
+// the running totals carried across rows -- lane 15 of rows 0 and 2 into rows
+// 1 and 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan_int(int v) {
+    v += dpp_i0<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_i0<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_i0<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_i0<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_i0<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp_i0<0x143, 0xC>(v);  // row_bcast:31
     return v;
 }
 
-__device__ __forceinline__ int wave_incl_scan_int(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
+// Sum over the 64 lanes (wave-uniform result).
+__device__ __forceinline__ int wave_sum_int(int v) { return __builtin_amdgcn_readlane(wave_incl_scan_int(v), 63); }
+
+// floor(num / den) for 0 <= num < 2^53 and 0 < den < 2^53: the correctly
+// rounded double quotient is within one of it, and one step corrects it.
+__device__ __forceinline__ int64_t div_floor(int64_t num, int64_t den) {
+    int64_t q = (int64_t)((double)num / (double)den);
+    if (q * den > num) {
+        --q;
+    } else if ((q + 1) * den <= num) {
+        ++q;
     }
-    return v;
+    return q;
 }
 
 __device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {
