@@ -36,9 +36,8 @@
 // the segment's units writes a record per tile to LDS (element offset of the
 // tile in the pools, valid rows, first/last/bad flags) with all block-table
 // entries and q rows fetched by the lanes at once; the tile loop then reads
-// one LDS record per tile.  Tile buffers form a ring: the loads of tiles
-// t + 1 and t + 2 (t + 1 only, for G = 8) are in flight while tile t is
-// computed.
+// one LDS record per tile.  Two tile buffers alternate: the loads of tile
+// t + 1 are in flight while tile t is computed.
 #include <math.h>
 
 #include <map>
@@ -250,11 +249,50 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     int useq_base = 0;           // global index of its sequence's first tile
     int ustart = 0;              // first token of its sequence covered here
 
-    // Leave the current unit: write its output (the wave saw every tile of it)
-    // or a partial result at slot unit + wave; the wave that saw the unit's
-    // first tile records where the unit's partials start and how many there
+    // Leave the current unit: its output (the wave saw every tile of it) or a
+    // partial result for slot unit + wave; the wave that saw the unit's first
+    // tile also records where the unit's partials start and how many there
     // are (waves from the one holding its first tile to the one holding its
-    // last), for the merge kernel.
+    // last), for the merge kernel.  Results are staged in LDS and stored
+    // together when the wave's run of tiles ends: a global store issued in
+    // the middle of the run would hold back every load issued after it (the
+    // memory counter retires in order), and under full read traffic a store
+    // takes as long to be acknowledged as a tile takes to arrive.  A full
+    // stage is flushed early.
+    // Stage depth: what fits next to the other tables in 20 KB of LDS per
+    // workgroup (eight workgroups per CU).
+    constexpr int kStage = START ? (G == 1 ? 10 : G == 2 ? 5 : G == 4 ? 2 : 1)
+                                 : (G == 1 ? 12 : G == 2 ? 6 : G == 4 ? 3 : 1);
+    __shared__ float4 stage_acc[kStage][G * 32];  // result rows as stored: head h, dims 4f .. 4f + 3 at h * 32 + f
+    __shared__ float2 stage_ml[kStage][G];        // partials: (m, l) per head
+    __shared__ int4 stage_meta[kStage];           // partial?, unit, slot, record count (0: no record)
+    int nstage = 0;                               // wave-uniform
+
+    // Store the staged results: each one's G rows are G * 128 contiguous
+    // floats of out (a finished unit) or of the partial slots; all 64 lanes
+    // move 16 bytes per store.
+    auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int r = 0; r < nstage; ++r) {
+            const int4 md = stage_meta[r];
+            const bool part = __builtin_amdgcn_readfirstlane(md.x) != 0;
+            const int64_t su = __builtin_amdgcn_readfirstlane(md.y);
+            const int64_t sslot = __builtin_amdgcn_readfirstlane(md.z);
+            const int rcount = __builtin_amdgcn_readfirstlane(md.w);
+            float4* dst = reinterpret_cast<float4*>(part ? a.ws_acc + sslot * G * kHd : a.out + su * G * kHd);
+#pragma unroll
+            for (int f = lane; f < G * 32; f += kWave) dst[f] = stage_acc[r][f];
+            if (part && lane < G) a.ws_ml[sslot * G + lane] = stage_ml[r][lane];
+            if (rcount != 0 && lane == 0) a.ws_rec[su] = make_int2((int)sslot, rcount);
+        }
+        nstage = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
     auto finish_unit = [&](bool unit_end) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -267,40 +305,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int r = 0; r < 4; ++r) lsum[r] = row_sum16(l[r]);
         const int64_t u = (int64_t)ui * Hkv + ug;
-        if (from_start && unit_end && !(START && ustart != 0)) {
-            if (lane < 16) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float inv = bad ? NAN : 1.f / read_lane(lsum[h & 3], 16 * (h >> 2));
-                    float4* o = reinterpret_cast<float4*>(
-                        a.out + ((int64_t)ui * Hq + (int64_t)ug * G + h) * kHd + 8 * lane);
-                    o[0] = make_float4(acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv);
-                    o[1] = make_float4(acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv);
-                }
-            }
-            if (lane == 0) a.ws_rec[u] = make_int2((int)(u + w), 1);
-            return;
-        }
         const int64_t slot = u + w;
+        const bool whole = from_start && unit_end && !(START && ustart != 0);
+        if (nstage == kStage) flush();
+        const int r = nstage;
+        if (whole) {  // normalise in place (the accumulator is reset at the next unit)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float inv = bad ? NAN : 1.f / read_lane(lsum[h & 3], 16 * (h >> 2));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= inv;
+            }
+        }
         if (lane < 16) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                float4* pa = reinterpret_cast<float4*>(a.ws_acc + (slot * G + h) * kHd + 8 * lane);
-                pa[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-                pa[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+                stage_acc[r][h * 32 + 2 * lane] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+                stage_acc[r][h * 32 + 2 * lane + 1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
             }
         }
+        int rcount = whole ? 1 : 0;
+        if (!whole) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
-            const float mh = read_lane(m[h & 3], 16 * (h >> 2));
-            if (lane == h) a.ws_ml[slot * G + h] = make_float2(mh, bad ? NAN : lh);
+            for (int h = 0; h < G; ++h) {
+                const float lh = read_lane(lsum[h & 3], 16 * (h >> 2));
+                const float mh = read_lane(m[h & 3], 16 * (h >> 2));
+                if (lane == h) stage_ml[r][h] = make_float2(mh, bad ? NAN : lh);
+            }
+            if (from_start) {
+                const int64_t last_tile = (int64_t)useq_base + (int64_t)ug * un + un - 1;
+                const int64_t w_last = div_floor((last_tile + 1) * W - 1, Nt);
+                rcount = (int)(w_last - w + 1);
+            }
         }
-        if (from_start && lane == 0) {
-            const int64_t last_tile = (int64_t)useq_base + (int64_t)ug * un + un - 1;
-            const int64_t w_last = div_floor((last_tile + 1) * W - 1, Nt);
-            a.ws_rec[u] = make_int2((int)slot, (int)(w_last - w + 1));
-        }
+        if (lane == 0) stage_meta[r] = make_int4(whole ? 0 : 1, (int)u, (int)slot, rcount);
+        nstage = r + 1;
     };
 
     for (int64_t seg0 = c0; seg0 < c1;) {
@@ -526,53 +565,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             if (unit_end || t + 1 == c1) finish_unit(unit_end);
         };
 
-        // Tile buffers in a ring: while tile kk is computed, the next tiles
-        // are in flight (two of them for G <= 4; for G = 8 the wider
-        // accumulator leaves room for one).  Every phase issues exactly one
-        // tile's loads (past the end of the segment it requests its last tile
-        // again, which the cache holds), so all paths issue the same loads in
-        // the same order and each wait counts exactly the loads it needs.
-        // The scheduling barriers keep every tile's loads in issue order: if
-        // the compiler interleaves the loads of two tiles, the wait counts it
-        // derives at the loop head have to cover both, and the ring drains.
-        if constexpr (G <= 4) {
-            auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
-                if (kk < seg_len) begin(seg0 + kk, cur);
-                __builtin_amdgcn_sched_barrier(0);
-                issue(min(kk + 2, seg_len - 1), ahead);
-                __builtin_amdgcn_sched_barrier(0);
-                if (kk < seg_len) step(seg0 + kk, cur);
-            };
-            TileLoad X0, X1, X2;
-            issue(0, X0);
+        // Two tile buffers: while tile kk is computed, the loads of tile kk + 1
+        // are in flight.  (A third buffer, two tiles ahead, measured no faster:
+        // the chip's read queues are already full with one tile ahead per
+        // wave.)  Every phase issues exactly one tile's loads (past the end of
+        // the segment it requests its last tile again, which the cache holds),
+        // so all paths issue the same loads in the same order and each wait
+        // counts exactly the loads it needs.  The scheduling barriers keep
+        // every tile's loads in issue order: if the compiler interleaves the
+        // loads of two tiles, the wait counts it derives at the loop head have
+        // to cover both, and the pipeline drains.
+        auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
+            if (kk < seg_len) begin(seg0 + kk, cur);
             __builtin_amdgcn_sched_barrier(0);
-            issue(min(1, seg_len - 1), X1);
+            issue(min(kk + 1, seg_len - 1), ahead);
             __builtin_amdgcn_sched_barrier(0);
-            for (int kk = 0; kk < seg_len; kk += 3) {
-                phase(kk, X0, X2);
-                phase(kk + 1, X1, X0);
-                phase(kk + 2, X2, X1);
-            }
-        } else {
-            auto phase = [&](int kk, TileLoad& cur, TileLoad& ahead) {
-                if (kk < seg_len) begin(seg0 + kk, cur);
-                __builtin_amdgcn_sched_barrier(0);
-                issue(min(kk + 1, seg_len - 1), ahead);
-                __builtin_amdgcn_sched_barrier(0);
-                if (kk < seg_len) step(seg0 + kk, cur);
-            };
-            TileLoad X0, X1;
-            issue(0, X0);
-            __builtin_amdgcn_sched_barrier(0);
-            for (int kk = 0; kk < seg_len; kk += 2) {
-                phase(kk, X0, X1);
-                phase(kk + 1, X1, X0);
-            }
+            if (kk < seg_len) step(seg0 + kk, cur);
+        };
+        TileLoad X0, X1;
+        issue(0, X0);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < seg_len; kk += 2) {
+            phase(kk, X0, X1);
+            phase(kk + 1, X1, X0);
         }
         seg0 += seg_len;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
+    flush();
 }
 
 // Merge kernel: one workgroup per (sequence, KV head) unit, one wave per query
