@@ -59,9 +59,6 @@ def parse_args(argv=None):
     p.add_argument("--prefix", action="store_true",
                    help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
                         "each shared block is read once per group")
-    p.add_argument("--event-stride", type=int, default=8,
-                   help="record per-launch timing events on every n-th timed step only: each event "
-                        "between two kernels leaves the stream idle for a few microseconds")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -265,40 +262,52 @@ class _HipEvents:
                 self.lib.hipEventDestroy(e)
 
 
-def timed_steps(write, decode, K: int, stride: int) -> dict:
-    """Run K steps of write() then decode() between two synchronisations.  Per-launch events
-    bracket write and decode on every stride-th step only (on the current stream, where both
-    launch); one event pair brackets the whole region for its GPU-clock length."""
-    stride = max(1, stride)
-    sampled = list(range(0, K, stride))
+def timed_steps(write, decode, K: int) -> dict:
+    """The timed region: K steps of write() then decode() between two synchronisations, with
+    nothing between the kernels (an event between two kernels idles the stream for
+    microseconds).  Then the per-launch durations: K decode launches back to back, and K write
+    launches back to back, each run bracketed by one pair of HIP events on the current stream
+    (where both launch), so each figure is the run's length over K."""
     he = _HipEvents()
-    ev = {i: [he.new() for _ in range(3)] for i in sampled}
     whole = [he.new() for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     he.record(whole[0])
-    for i in range(K):
-        e = ev.get(i)
-        if e:
-            he.record(e[0])
+    for _ in range(K):
         write()
-        if e:
-            he.record(e[1])
         decode()
-        if e:
-            he.record(e[2])
     he.record(whole[1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+
+    def per_launch(fn, lead: int = 0) -> float:
+        # `lead` decode calls go first so that the GPU is still busy while the host queues K
+        # short launches: a kernel shorter than its host-side call would otherwise be timed
+        # with the host's gaps between launches.
+        e = [he.new() for _ in range(2)]
+        torch.cuda.synchronize()
+        for _ in range(lead):
+            decode()
+        he.record(e[0])
+        for _ in range(K):
+            fn()
+        he.record(e[1])
+        torch.cuda.synchronize()
+        ms = he.elapsed_ms(e[0], e[1]) / K
+        he.free(e)
+        return ms
+
+    decode_ms = per_launch(decode)
+    # ~20 us of host time per queued write, covered by decode calls in front.
+    lead = min(1000, int(K * 0.02 / max(decode_ms, 1e-3)) + 2)
     res = {
         "ms_per_step": (t1 - t0) * 1e3 / K,
         "gpu_ms_per_step": he.elapsed_ms(whole[0], whole[1]) / K,
-        "write_ms": [he.elapsed_ms(ev[i][0], ev[i][1]) for i in sampled],
-        "decode_ms": [he.elapsed_ms(ev[i][1], ev[i][2]) for i in sampled],
+        "decode_ms": decode_ms,
+        "write_ms": per_launch(write, lead),
         "event_kind": he.kind,
-        "event_stride": stride,
     }
-    he.free([x for v in ev.values() for x in v] + whole)
+    he.free(whole)
     return res
 
 
@@ -337,9 +346,9 @@ def bench_multi(args) -> int:
         attend()
     torch.cuda.synchronize()
     K = args.steps
-    tm = timed_steps(write, attend, K, args.event_stride)
+    tm = timed_steps(write, attend, K)
     ms_per_step = tm["ms_per_step"]
-    att = statistics.mean(tm["decode_ms"]) * 1e-3
+    att = tm["decode_ms"] * 1e-3
     ctx = w.context_lens.astype(np.int64)
     ql = np.diff(w.cu_q).astype(np.int64)
     kv = int(ctx.sum()) * 2 * w.num_kv_heads * w.head_dim * w.elem_bytes
@@ -363,10 +372,9 @@ def bench_multi(args) -> int:
         "attention_us": att * 1e6,
         "mfma_TFLOPs": flops / att / 1e12,
         "mfma_frac_of_bf16_peak": flops / att / 2.5e15,
-        "write_us": statistics.mean(tm["write_ms"]) * 1e3,
-        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "event_stride": tm["event_stride"],
-                   "events": tm["event_kind"],
-                   "sampled_launches": len(tm["decode_ms"])},
+        "write_us": tm["write_ms"] * 1e3,
+        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "events": tm["event_kind"],
+                   "per_launch": "K launches back to back / K"},
     }
     if not args.no_parity:
         import oracle
@@ -458,12 +466,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    tm = timed_steps(write, decode, K, args.event_stride)
+    tm = timed_steps(write, decode, K)
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
     ms_per_step = tm["ms_per_step"]
-    write_ms = tm["write_ms"]
-    decode_ms = tm["decode_ms"]
-    dec_avg = statistics.mean(decode_ms)
+    dec_avg = tm["decode_ms"]
     nbytes = algorithmic_bytes(w)
     # The prefix path has to move each shared block once: it is priced on the unique bytes.
     moved = nbytes["total_unique"] if args.prefix else nbytes["total"]
@@ -521,11 +527,9 @@ def main(argv=None) -> int:
         "kv_unique_GBps": nbytes["kv_unique"] / (dec_avg * 1e-3) / 1e9,
         "kv_read_pct_of_peak": 100.0 * kv_gbs / PEAK_HBM_GBS,
         "decode_us": dec_avg * 1e3,
-        "decode_us_min": min(decode_ms) * 1e3,
-        "write_us": statistics.mean(write_ms) * 1e3,
-        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "event_stride": tm["event_stride"],
-                   "events": tm["event_kind"],
-                   "sampled_launches": len(decode_ms)},
+        "write_us": tm["write_ms"] * 1e3,
+        "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "events": tm["event_kind"],
+                   "per_launch": "K launches back to back / K"},
         "algorithmic_bytes": nbytes,
         "gpu": torch.cuda.get_device_name(0),
         "torch": torch.__version__,

@@ -298,8 +298,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                acc[h][e] += __shfl_xor(acc[h][e], 16, kWave);
-                acc[h][e] += __shfl_xor(acc[h][e], 32, kWave);
+                acc[h][e] = sum_xor32(sum_xor16(acc[h][e]));
             }
         float lsum[4];
 #pragma unroll
@@ -843,8 +842,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
         }
         if (__any(need)) {
             float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+            tm = max_xor32(max_xor16(tm));
             const float mn = tm > m + kLazyRescale ? tm : m;
             const float alpha = fast_exp2(m - mn);
             m = mn;
@@ -905,8 +903,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
     }
 
     if (!computes) return;
-    float lt = l + __shfl_xor(l, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    const float lt = sum_xor32(sum_xor16(l));
     // Row r of the wave is member r / G, head r % G.  A member writes chunk c
     // when its own prefix has that chunk; its rows are NaN when its prefix
     // disagrees with the group's or does not fit its sequence.
@@ -1070,8 +1067,7 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
         }
         if (__any(need)) {
             float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+            tm = max_xor32(max_xor16(tm));
             const float mn = tm > m + kLazyRescale ? tm : m;
             const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
             m = mn;
@@ -1126,8 +1122,7 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
     }
 
     if (!computes) return;
-    float lt = l + __shfl_xor(l, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    const float lt = sum_xor32(sum_xor16(l));
     const int MC = a.prefix_max_chunks;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {

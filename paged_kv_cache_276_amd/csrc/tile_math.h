@@ -38,6 +38,29 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// Pairwise combines across 16-lane rows without LDS, by the gfx950 lane-swap
+// moves.  v_permlane16_swap given two copies of v returns (rows 0,0,2,2 of v;
+// rows 1,1,3,3 of v), so combining the two gives every lane l the pair
+// {v[l], v[l ^ 16]}; v_permlane32_swap does the same for the two halves,
+// {v[l], v[l ^ 32]}.  Both lanes of a pair combine the same two values in
+// the same order, so they agree bit for bit.
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // DPP move of an int where lanes without a source, and lanes of rows outside
 // ROW_MASK, read 0.
 template <int CTRL, int ROW_MASK>
