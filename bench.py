@@ -50,6 +50,8 @@ def parse_args(argv=None):
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kernel", type=int, default=0, help="0 auto, 1 generic, 2 fast")
     p.add_argument("--grid-waves", type=int, default=0, help="fast kernel: waves sharing the work (0 = library choice)")
+    p.add_argument("--xcd-balance", type=int, default=0,
+                   help="fast kernel: share of a wave on an odd XCD in 64ths (64 = equal, 0 = library choice)")
     p.add_argument("--cold-steps", type=int, default=10,
                    help="after the timed steps, time this many decode calls each preceded by "
                         "reading --flush-mib of scratch (no KV bytes left in L2 or MALL)")
@@ -435,14 +437,14 @@ def main(argv=None) -> int:
         max_prefix = int(start.max())
         plan = pkv.paged_attn_prefix_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, len(grows), max_prefix,
                                           d["k_cache"], chunk_tokens=args.partition_tokens,
-                                          grid_waves=args.grid_waves)
+                                          grid_waves=args.grid_waves, xcd_balance=args.xcd_balance)
         plan["partition_tokens"] = plan["chunk_tokens"]
         plan["grid_blocks"] = args.grid_waves
         plan["kernel"] = "prefix"
     else:
         plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"],
                                    partition_tokens=args.partition_tokens, kernel=args.kernel,
-                                   grid_waves=args.grid_waves)
+                                   grid_waves=args.grid_waves, xcd_balance=args.xcd_balance)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = torch.empty((max(plan["workspace_bytes"], 16) + 15) // 16 * 16, dtype=torch.uint8, device=dev)
 
@@ -453,11 +455,12 @@ def main(argv=None) -> int:
         if args.prefix:
             pkv.paged_attn_decode_prefix(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                                          d["seq_prefix"], d["groups"], max_prefix, w.scale, out=out, workspace=ws,
-                                         chunk_tokens=args.partition_tokens, grid_waves=args.grid_waves)
+                                         chunk_tokens=args.partition_tokens, grid_waves=args.grid_waves,
+                                         xcd_balance=args.xcd_balance)
         else:
             pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                                   w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
-                                  kernel=args.kernel, grid_waves=args.grid_waves)
+                                  kernel=args.kernel, grid_waves=args.grid_waves, xcd_balance=args.xcd_balance)
 
     print(f"[bench] warmup {args.warmup} steps, plan {plan}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -512,6 +515,7 @@ def main(argv=None) -> int:
             "kernel": plan["kernel"],
             "partition_tokens": plan["partition_tokens"],
             "grid_waves": plan["grid_blocks"],
+            "xcd_balance": args.xcd_balance or pkv.XCD_BALANCE_DEFAULT,
         },
         "roofline": {
             "kernel": ("paged_attn_decode_prefix (prefix, suffix and merge kernels, one call; unique bytes)"

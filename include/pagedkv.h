@@ -92,7 +92,18 @@ typedef struct pkv_decode_opts {
     int32_t kernel;           /* a PKV_KERNEL_* value */
     int32_t grid_waves;       /* fast kernel: number of waves that share the work, 1 ..
                                  PKV_MAX_GRID_WAVES; 0 = as many as the device keeps resident */
+    int32_t xcd_balance;      /* fast kernel: work share of each wave on an odd-numbered XCD, in
+                                 64ths of an equal share (waves on even XCDs get 128 minus it),
+                                 1 .. 127; 64 = equal shares; 0 = library choice
+                                 (PKV_XCD_BALANCE_DEFAULT).  Applies when the wave count is a
+                                 multiple of 8 and there are at least as many tiles as waves;
+                                 results do not depend on it. */
 } pkv_decode_opts;
+
+/* On the MI355X boxes measured, waves on odd-numbered XCDs drained the same reads 4-9% more
+ * slowly than waves on even ones, so an equal split left the odd XCDs finishing last; their
+ * waves get this share (in 64ths) by default. */
+#define PKV_XCD_BALANCE_DEFAULT 60
 
 /* Upper bound of the fast kernel's wave count (sizes its workspace). */
 #define PKV_MAX_GRID_WAVES 8192

@@ -73,8 +73,13 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(nb, b, hkv, d, _DTYPES[k_cache.dtype])
 
 
-def _opts(partition_tokens: int, kernel: int, grid_waves: int = 0) -> DecodeOpts:
-    return DecodeOpts(int(partition_tokens), int(kernel), int(grid_waves))
+# Default share (in 64ths of an equal share) of the fast kernel's waves on odd-numbered XCDs;
+# the same value as PKV_XCD_BALANCE_DEFAULT in include/pagedkv.h.
+XCD_BALANCE_DEFAULT = 60
+
+
+def _opts(partition_tokens: int, kernel: int, grid_waves: int = 0, xcd_balance: int = 0) -> DecodeOpts:
+    return DecodeOpts(int(partition_tokens), int(kernel), int(grid_waves), int(xcd_balance))
 
 
 def _need(cond: bool, msg: str) -> None:
@@ -133,12 +138,12 @@ def paged_block_copy(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.
 
 def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
                     partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
-                    grid_waves: int = 0) -> Dict[str, int]:
+                    grid_waves: int = 0, xcd_balance: int = 0) -> Dict[str, int]:
     """Host-only launch plan (kernel family, partition size, grid, workspace bytes)."""
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     plan = DecodePlan()
     st = _lib.lib().paged_attn_plan(num_seqs, num_q_heads, max_blocks_per_seq, ctypes.byref(desc),
-                                    ctypes.byref(_opts(partition_tokens, kernel, grid_waves)),
+                                    ctypes.byref(_opts(partition_tokens, kernel, grid_waves, xcd_balance)),
                                     ctypes.byref(plan))
     _lib.check(st, "paged_attn_plan")
     return {
@@ -153,12 +158,12 @@ def paged_attn_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, ca
 
 def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, cache,
                                partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
-                               grid_waves: int = 0) -> int:
+                               grid_waves: int = 0, xcd_balance: int = 0) -> int:
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     out = ctypes.c_uint64(0)
     st = _lib.lib().paged_attn_workspace_bytes(num_seqs, num_q_heads, max_blocks_per_seq,
                                                ctypes.byref(desc),
-                                               ctypes.byref(_opts(partition_tokens, kernel, grid_waves)),
+                                               ctypes.byref(_opts(partition_tokens, kernel, grid_waves, xcd_balance)),
                                                ctypes.byref(out))
     _lib.check(st, "paged_attn_workspace_bytes")
     return int(out.value)
@@ -184,7 +189,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                       partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
-                      grid_waves: int = 0, stream=None) -> torch.Tensor:
+                      grid_waves: int = 0, xcd_balance: int = 0, stream=None) -> torch.Tensor:
     """out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i over the paged K/V of sequence i (fp32)."""
     dev = k_cache.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
@@ -204,9 +209,9 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _dev(out, "out", dev)
     _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
     maxb = block_tables.shape[1]
-    opts = _opts(partition_tokens, kernel, grid_waves)
+    opts = _opts(partition_tokens, kernel, grid_waves, xcd_balance)
     s = _stream(dev, stream)
-    plan = paged_attn_plan(S, Hq, maxb, desc, partition_tokens, kernel, grid_waves)
+    plan = paged_attn_plan(S, Hq, maxb, desc, partition_tokens, kernel, grid_waves, xcd_balance)
     need = plan["workspace_bytes"]
     if workspace is None:
         workspace = _workspace(dev, int(s.value or 0), need)
@@ -225,13 +230,14 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
 
 
 def paged_attn_prefix_plan(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, num_groups: int,
-                           max_prefix_tokens: int, cache, chunk_tokens: int = 0, grid_waves: int = 0) -> Dict[str, int]:
+                           max_prefix_tokens: int, cache, chunk_tokens: int = 0, grid_waves: int = 0,
+                           xcd_balance: int = 0) -> Dict[str, int]:
     """Host-only plan of the shared-prefix decode (prefix chunk, chunks, workspace bytes)."""
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     plan = DecodePlan()
     st = _lib.lib().paged_attn_prefix_plan(num_seqs, num_q_heads, max_blocks_per_seq, num_groups,
                                            max_prefix_tokens, ctypes.byref(desc),
-                                           ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)),
+                                           ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves, xcd_balance)),
                                            ctypes.byref(plan))
     _lib.check(st, "paged_attn_prefix_plan")
     return {"kernel": KERNEL_NAMES.get(plan.kernel, str(plan.kernel)), "chunk_tokens": plan.partition_tokens,
@@ -243,7 +249,7 @@ def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                              seq_prefix_tokens: torch.Tensor, groups: torch.Tensor, max_prefix_tokens: int,
                              scale: float, out: Optional[torch.Tensor] = None,
                              workspace: Optional[torch.Tensor] = None, chunk_tokens: int = 0,
-                             grid_waves: int = 0, stream=None) -> torch.Tensor:
+                             grid_waves: int = 0, xcd_balance: int = 0, stream=None) -> torch.Tensor:
     """paged_attn_decode for groups of sequences sharing prefix blocks; each shared block is read once per group."""
     dev = k_cache.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
@@ -265,7 +271,7 @@ def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
     maxb = block_tables.shape[1]
     G = groups.shape[0]
-    plan = paged_attn_prefix_plan(S, Hq, maxb, G, max_prefix_tokens, desc, chunk_tokens, grid_waves)
+    plan = paged_attn_prefix_plan(S, Hq, maxb, G, max_prefix_tokens, desc, chunk_tokens, grid_waves, xcd_balance)
     s = _stream(dev, stream)
     need = plan["workspace_bytes"]
     if workspace is None:
@@ -279,7 +285,7 @@ def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         ctypes.c_void_p(seq_prefix_tokens.data_ptr()), ctypes.c_void_p(groups.data_ptr()), G,
         int(max_prefix_tokens), ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), ctypes.byref(desc),
-        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)), s)
+        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves, xcd_balance)), s)
     _lib.check(st, "paged_attn_decode_prefix")
     return out
 

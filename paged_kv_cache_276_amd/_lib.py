@@ -58,7 +58,7 @@ class CacheDesc(ctypes.Structure):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("grid_waves", ctypes.c_int32)]
+                ("grid_waves", ctypes.c_int32), ("xcd_balance", ctypes.c_int32)]
 
 
 class DecodePlan(ctypes.Structure):

@@ -93,6 +93,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
 
     const int32_t waves = opts ? opts->grid_waves : 0;
     if (waves < 0 || waves > pkv::kMaxGridWaves) return PKV_ERR_SHAPE;
+    if (opts && (opts->xcd_balance < 0 || opts->xcd_balance > 127)) return PKV_ERR_SHAPE;
 
     if (kernel == PKV_KERNEL_FAST) {
         plan->kernel = kernel;
@@ -218,6 +219,7 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
     a.part_tokens = plan.partition_tokens;
     a.max_parts = plan.max_partitions;
     a.grid_waves = opts ? opts->grid_waves : 0;
+    a.xcd_balance = opts && opts->xcd_balance ? opts->xcd_balance : PKV_XCD_BALANCE_DEFAULT;
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -342,6 +344,7 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
     a.part_tokens = 16;
     a.max_parts = pkv::kMaxGridWaves;
     a.grid_waves = opts ? opts->grid_waves : 0;
+    a.xcd_balance = opts && opts->xcd_balance ? opts->xcd_balance : PKV_XCD_BALANCE_DEFAULT;
     a.seq_start = seq_prefix_tokens;
     a.groups = groups;
     a.num_groups = num_groups;

@@ -146,8 +146,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (Nt == 0) return;
     const int W = (int)(Nt < nwaves ? Nt : nwaves);
     if (w >= W) return;
-    const int64_t c0 = div_floor((int64_t)w * Nt, W);
-    const int64_t c1 = div_floor((int64_t)(w + 1) * Nt, W);
+    const Split sp = make_split(Nt, W, nwaves, a.xcd_balance);
+    const int64_t c0 = sp.start(w);
+    const int64_t c1 = sp.start(w + 1);
 
     // ---- 2. the sequence holding tile c0
     int i0 = -1;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             }
             if (from_start) {
                 const int64_t last_tile = (int64_t)useq_base + (int64_t)ug * un + un - 1;
-                const int64_t w_last = div_floor((last_tile + 1) * W - 1, Nt);
+                const int64_t w_last = sp.wave_of(last_tile);
                 rcount = (int)(w_last - w + 1);
             }
         }

@@ -97,6 +97,53 @@ __device__ __forceinline__ int64_t div_floor(int64_t num, int64_t den) {
     return q;
 }
 
+// The fast kernel's split of Nt tiles over W waves.  Waves w = x * W8 + j
+// (j < W8) run on XCD x (workgroups are dealt to the eight XCDs in turn), and
+// a wave's share is wt(x) = b on odd x, 128 - b on even x, in 64ths of an
+// equal share.  S(w), the shares of the waves before w, is W8 * base(x) +
+// j * wt(x) with base(x) the shares of one wave of each XCD before x, so
+// S(W) = 64 W, and wave w takes tiles [floor(Nt S(w) / 64 W), floor(Nt
+// S(w + 1) / 64 W)).  W8 = 0 (or b = 64) is the equal split floor(Nt w / W).
+struct Split {
+    int64_t Nt;
+    int W;
+    int W8;
+    int b;
+    __device__ __forceinline__ int wt(int x) const { return (x & 1) ? b : 128 - b; }
+    __device__ __forceinline__ int64_t base(int x) const {
+        return (int64_t)(x >> 1) * 128 + ((x & 1) ? 128 - b : 0);
+    }
+    __device__ __forceinline__ int64_t S(int w) const {
+        if (W8 == 0) return 64ll * w;
+        const int x = w / W8;
+        return (int64_t)W8 * base(x) + (int64_t)(w - x * W8) * wt(x);
+    }
+    // First tile of wave w (w = W gives Nt).
+    __device__ __forceinline__ int64_t start(int w) const { return div_floor(Nt * S(w), 64ll * W); }
+    // The wave whose tiles include tile t: the last w with start(w) <= t, i.e.
+    // with S(w) <= T = floor(((t + 1) 64 W - 1) / Nt).
+    __device__ __forceinline__ int wave_of(int64_t t) const {
+        const int64_t T = div_floor((t + 1) * 64ll * W - 1, Nt);
+        if (W8 == 0) return (int)min<int64_t>(W - 1, T / 64);
+        int x = 7;
+        while (x > 0 && (int64_t)W8 * base(x) > T) --x;
+        const int64_t j = (T - (int64_t)W8 * base(x)) / wt(x);
+        return x * W8 + (int)min<int64_t>(W8 - 1, j);
+    }
+};
+
+// The split for W of the grid's waves.  XCD shares apply when W is the whole
+// grid, the grid is a whole number of waves per XCD, and the smaller share is
+// still at least one tile (Nt * min(b, 128 - b) >= 64 W): every wave below W
+// then owns a tile, so the waves that touch a unit are consecutive and each
+// leaves a partial result.
+__device__ __forceinline__ Split make_split(int64_t Nt, int W, int grid_waves, int balance) {
+    const int lo = balance < 128 - balance ? balance : 128 - balance;
+    const bool per_xcd = W == grid_waves && grid_waves % 8 == 0 && balance != 64 && balance > 0 &&
+                         balance < 128 && Nt * lo >= 64ll * W;
+    return Split{Nt, W, per_xcd ? grid_waves / 8 : 0, per_xcd ? balance : 64};
+}
+
 __device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {
     return (ctx < 0 || ctx > table_tokens) ? 0 : (ctx + kTok - 1) / kTok;
 }

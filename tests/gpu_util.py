@@ -37,7 +37,8 @@ def to_device(w, dev=None) -> Dict[str, torch.Tensor]:
 
 
 def run_step(w, partition_tokens: int = 0, kernel: int = 0, d: Optional[Dict[str, torch.Tensor]] = None,
-             write: bool = True, grid_waves: int = 0) -> Tuple[Dict[str, torch.Tensor], torch.Tensor]:
+             write: bool = True, grid_waves: int = 0,
+             xcd_balance: int = 0) -> Tuple[Dict[str, torch.Tensor], torch.Tensor]:
     import paged_kv_cache_276_amd as pkv
 
     d = d or to_device(w)
@@ -45,7 +46,7 @@ def run_step(w, partition_tokens: int = 0, kernel: int = 0, d: Optional[Dict[str
         pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
     out = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                                 w.scale, partition_tokens=partition_tokens, kernel=kernel,
-                                grid_waves=grid_waves)
+                                grid_waves=grid_waves, xcd_balance=xcd_balance)
     torch.cuda.synchronize()
     return d, out
 

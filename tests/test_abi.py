@@ -62,11 +62,11 @@ def _desc(nb=64, b=16, hkv=8, d=128, dtype=1):
     return CacheDesc(nb, b, hkv, d, dtype)
 
 
-def _plan(L, S, hq, maxb, desc, part=0, kernel=0, waves=0):
+def _plan(L, S, hq, maxb, desc, part=0, kernel=0, waves=0, xcd=0):
     from paged_kv_cache_276_amd import DecodeOpts, DecodePlan
 
     plan = DecodePlan()
-    st = L.paged_attn_plan(S, hq, maxb, ctypes.byref(desc), ctypes.byref(DecodeOpts(part, kernel, waves)),
+    st = L.paged_attn_plan(S, hq, maxb, ctypes.byref(desc), ctypes.byref(DecodeOpts(part, kernel, waves, xcd)),
                            ctypes.byref(plan))
     return st, plan
 
@@ -110,6 +110,20 @@ def test_plan_fast_kernel(L):
     assert st == 0 and plan.grid_blocks == 100
     assert _plan(L, 4, 32, 16, _desc(), waves=8193)[0] == 2
     assert _plan(L, 4, 32, 16, _desc(), waves=-1)[0] == 2
+
+
+def test_plan_xcd_balance(L):
+    """The odd-XCD share is 1..127 in 64ths (0 = library choice); anything else is refused, and the
+    library's default is the header's PKV_XCD_BALANCE_DEFAULT, mirrored in the binding."""
+    import paged_kv_cache_276_amd as pkv
+
+    for ok in (0, 1, 62, 64, 127):
+        assert _plan(L, 4, 32, 16, _desc(), xcd=ok)[0] == 0, ok
+    for bad in (-1, 128, 1000):
+        assert _plan(L, 4, 32, 16, _desc(), xcd=bad)[0] == 2, bad
+    with open(os.path.join(ROOT, "include", "pagedkv.h")) as f:
+        m = re.search(r"#define\s+PKV_XCD_BALANCE_DEFAULT\s+(\d+)", f.read())
+    assert m and int(m.group(1)) == pkv.XCD_BALANCE_DEFAULT
 
 
 @pytest.mark.parametrize(

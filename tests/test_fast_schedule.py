@@ -1,7 +1,7 @@
 """Host model of the fast decode kernel's work split (its integer arithmetic, step by step).
 
-The kernel gives wave w the tiles [w*Nt/W, (w+1)*Nt/W) of all (sequence, KV head,
-16-token tile) triples, finds its first sequence with a two-level prefix sum
+The kernel gives wave w the tiles [start(w), start(w+1)) of all (sequence, KV head,
+16-token tile) triples -- equal shares, or shares weighted by the wave's XCD -- finds its first sequence with a two-level prefix sum
 (8 sequences per lane, 64 lanes, ballot), walks the tiles with a cursor, keeps
 partial results at slot unit + w, and the wave that sees a unit's first tile
 records (first slot, count) with count = wave_of(last tile) - w + 1.  This model
@@ -88,7 +88,68 @@ def segment_walk(ctx, hkv, block_size, max_blocks, c0, c1, cur, seg_runs):
         seg0 += seg_len
 
 
-def run_schedule(ctx, hkv, block_size, max_blocks, nwaves, seg_runs=8):
+class Split:
+    """The kernel's work split (tile_math.h, Split and make_split), integer for integer."""
+
+    def __init__(self, Nt, W, grid_waves, balance):
+        lo = min(balance, 128 - balance)
+        per_xcd = (W == grid_waves and grid_waves % 8 == 0 and balance != 64 and 0 < balance < 128
+                   and Nt * lo >= 64 * W)
+        self.Nt, self.W = Nt, W
+        self.W8 = grid_waves // 8 if per_xcd else 0
+        self.b = balance if per_xcd else 64
+
+    def wt(self, x):
+        return self.b if x & 1 else 128 - self.b
+
+    def base(self, x):
+        return (x >> 1) * 128 + ((128 - self.b) if x & 1 else 0)
+
+    def S(self, w):
+        if self.W8 == 0:
+            return 64 * w
+        x = w // self.W8
+        return self.W8 * self.base(x) + (w - x * self.W8) * self.wt(x)
+
+    def start(self, w):
+        return (self.Nt * self.S(w)) // (64 * self.W)
+
+    def wave_of(self, t):
+        T = ((t + 1) * 64 * self.W - 1) // self.Nt
+        if self.W8 == 0:
+            return min(self.W - 1, T // 64)
+        x = 7
+        while x > 0 and self.W8 * self.base(x) > T:
+            x -= 1
+        return x * self.W8 + min(self.W8 - 1, (T - self.W8 * self.base(x)) // self.wt(x))
+
+
+def test_split_inverse_and_nonempty_waves():
+    """wave_of inverts start, every wave below W owns a tile, and the shares follow the XCDs."""
+    rng = np.random.default_rng(3)
+    for _ in range(400):
+        grid = int(rng.choice([8, 16, 64, 256, 2048, 2056, 24, 7]))
+        Nt = int(rng.integers(1, 40 * grid))
+        W = min(Nt, grid)
+        b = int(rng.choice([1, 10, 40, 61, 62, 64, 70, 100, 127]))
+        sp = Split(Nt, W, grid, b)
+        starts = [sp.start(w) for w in range(W + 1)]
+        assert starts[0] == 0 and starts[W] == Nt
+        assert all(starts[w + 1] > starts[w] for w in range(W)), (grid, Nt, b)
+        for t in rng.integers(0, Nt, 50):
+            w = sp.wave_of(int(t))
+            assert starts[w] <= t < starts[w + 1]
+        if sp.W8 and Nt >= 100 * W:  # shares come out as asked, to within a tile
+            for w in (0, sp.W8, 2 * sp.W8 + 1, 3 * sp.W8):
+                x = w // sp.W8
+                want = Nt * sp.wt(x) / (64 * W)
+                assert abs((starts[w + 1] - starts[w]) - want) <= 1
+    # equal shares reduce to floor(Nt w / W)
+    sp = Split(202792, 2048, 2048, 64)
+    assert [sp.start(w) for w in range(0, 2049, 97)] == [w * 202792 // 2048 for w in range(0, 2049, 97)]
+
+
+def run_schedule(ctx, hkv, block_size, max_blocks, nwaves, seg_runs=8, balance=64):
     table_tokens = max_blocks * block_size
     S = len(ctx)
     n = [tiles_of(c, table_tokens) for c in ctx]
@@ -107,7 +168,8 @@ def run_schedule(ctx, hkv, block_size, max_blocks, nwaves, seg_runs=8):
         seen_w.add(w)
         if w >= W:
             continue
-        c0, c1 = w * Nt // W, (w + 1) * Nt // W
+        sp = Split(Nt, W, nwaves, balance)
+        c0, c1 = sp.start(w), sp.start(w + 1)
         assert c1 > c0, "every wave below W owns at least one tile"
         i, base = locate(ctx, table_tokens, hkv, c0)
         assert 0 <= i < S
@@ -144,7 +206,7 @@ def run_schedule(ctx, hkv, block_size, max_blocks, nwaves, seg_runs=8):
                     slots[slot] = (u, w)
                 if from_start:
                     last_tile = cur["seq_base"] + g * cur["n"] + cur["n"] - 1
-                    w_last = ((last_tile + 1) * W - 1) // Nt
+                    w_last = sp.wave_of(last_tile)
                     records[u] = (u + w, w_last - w + 1)
                     assert (records[u][1] == 1) == complete
             # advance
@@ -193,8 +255,18 @@ def _cases():
 @pytest.mark.parametrize("seg_runs", [8, 4])
 @pytest.mark.parametrize("case", range(len(_cases())))
 def test_schedule_covers_every_tile_once(case, seg_runs):
+    _check_case(case, seg_runs, 64)
+
+
+@pytest.mark.parametrize("balance", [62, 20, 110])
+@pytest.mark.parametrize("case", range(len(_cases())))
+def test_schedule_with_xcd_shares(case, balance):
+    _check_case(case, 8, balance)
+
+
+def _check_case(case, seg_runs, balance):
     ctx, hkv, B, maxb, nwaves = _cases()[case]
-    Nt, visits, slots, records = run_schedule(ctx, hkv, B, maxb, nwaves, seg_runs)
+    Nt, visits, slots, records = run_schedule(ctx, hkv, B, maxb, nwaves, seg_runs, balance)
     assert len(visits) == Nt and all(v == 1 for v in visits.values())
     table_tokens = maxb * B
     touched = {}

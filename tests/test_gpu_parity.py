@@ -36,10 +36,11 @@ def _kernels_for(w):
     return ks
 
 
-def _check_step(w, oracle_impl, what, partition_tokens=0, kernel=0, grid_waves=0):
+def _check_step(w, oracle_impl, what, partition_tokens=0, kernel=0, grid_waves=0, xcd_balance=0):
     say(f"[gpu] {what}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"B={w.block_size} {w.dtype} T={partition_tokens} kernel={kernel} waves={grid_waves}")
-    d, out = run_step(w, partition_tokens=partition_tokens, kernel=kernel, grid_waves=grid_waves)
+        f"B={w.block_size} {w.dtype} T={partition_tokens} kernel={kernel} waves={grid_waves} xcd={xcd_balance}")
+    d, out = run_step(w, partition_tokens=partition_tokens, kernel=kernel, grid_waves=grid_waves,
+                      xcd_balance=xcd_balance)
     ref = oracle.decode_step(w, oracle=oracle_impl)
     assert np.array_equal(bits(d["k_cache"]), ref.k_cache_bits), f"{what}: K pool differs after write"
     assert np.array_equal(bits(d["v_cache"]), ref.v_cache_bits), f"{what}: V pool differs after write"
@@ -70,6 +71,18 @@ def test_fast_wave_count_sweep(waves, oracle_impl):
     _check_step(w, oracle_impl, f"waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
     w32 = make_custom([31, 32, 33, 64, 999], 8, 1, 128, 32, torch.bfloat16, seed=10, pool_fill=0.8)
     _check_step(w32, oracle_impl, f"waves{waves}/B32", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
+
+
+@pytest.mark.parametrize("balance", [1, 30, 62, 64, 100, 127])
+@pytest.mark.parametrize("waves", [8, 16, 64, 2048])
+def test_fast_xcd_balance(balance, waves, oracle_impl):
+    """Waves on odd XCDs take balance/64 of an equal share and even ones the rest (when every
+    wave keeps a tile): the split points and the merge records move, the results stay within
+    tolerance.  1592 tiles: at 64 waves balance 1 falls back to equal shares, 30 does not."""
+    w = make_custom([0, 1, 15, 16, 17, 100, 2000, 7, 4100, 33], 16, 4, 128, 16, torch.bfloat16, seed=9,
+                    pool_fill=0.8)
+    _check_step(w, oracle_impl, f"xcd{balance}/waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves,
+                xcd_balance=balance)
 
 
 SHAPES = [  # (lengths, Hq, Hkv, D, B, dtype)
