@@ -593,14 +593,25 @@ def main(argv=None) -> int:
     return 0
 
 
-def _kernel_source_sha() -> str:
+def _strip_comments(text: str) -> str:
+    """C/C++ source without comments and blank space, so that comment edits keep the stamp.
+    Naive about comment markers inside string literals, which the kernel sources do not use."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def _kernel_source_sha(csrc: str = None) -> str:
+    """Stamp of the kernel sources (their code, comments and layout excluded)."""
     import hashlib
 
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_cache_276_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "paged_kv_cache_276_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

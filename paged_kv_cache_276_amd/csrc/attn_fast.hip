@@ -3,12 +3,14 @@
 //
 // Work decomposition.  The unit of work is a tile: 16 consecutive logical
 // tokens of one (sequence, KV head).  All tiles are laid end to end in the
-// order (sequence, KV head, tile) and the grid's W waves each take an equal
+// order (sequence, KV head, tile) and the grid's W waves each take one
 // contiguous run of them (W = the waves the device keeps resident), so the
 // load is balanced whatever the length mix: a long sequence spreads over many
-// waves, many short ones share a wave.  Each wave finds its first tile from
-// the context lengths alone (two passes of a wave-wide prefix sum), so no host
-// synchronisation or planning kernel is needed.
+// waves, many short ones share a wave.  The runs are equal, or weighted by the
+// wave's XCD (odd XCDs read more slowly; Split in tile_math.h).  Each wave
+// finds its first tile from the context lengths alone (two passes of a
+// wave-wide prefix sum), so no host synchronisation or planning kernel is
+// needed.
 //
 // Per tile (4 KiB of K and 4 KiB of V for one KV head):
 //   * scores: the G query rows of the KV head (zero-padded to 16) times the 16
@@ -26,11 +28,12 @@
 //     4*i + l/16 (i = 0..3), i.e. each V load instruction reads 1 KiB
 //     contiguous; the weights p travel through 512 bytes of LDS.
 // When the wave leaves a (sequence, KV head) it folds the four lane groups,
-// then either normalises and writes the output rows (it saw every tile of the
-// unit) or stores (m, l, acc) as a partial result at slot unit + wave; the
-// wave that saw the unit's first tile records the unit's first slot and
-// partial count.  merge_fast_kernel then merges the partials with log-sum-exp
-// in slot order and writes the rows of sequences without tiles.
+// then stages either the normalised output rows (it saw every tile of the
+// unit) or (m, l, acc) as a partial result for slot unit + wave in LDS; the
+// stage is stored when the wave's run ends.  The wave that saw the unit's
+// first tile records the unit's first slot and partial count.
+// merge_fast_kernel then merges the partials with log-sum-exp in slot order
+// and writes the rows of sequences without tiles.
 //
 // Set-up per segment (up to 128 tiles and 8 pieces of units): one walk over
 // the segment's units writes a record per tile to LDS (element offset of the
