@@ -363,7 +363,7 @@ namespace {
 // head, 64-row block) and the chunk partials.
 struct MultiPlan {
     pkv_decode_plan base;
-    int32_t chunk_tiles, max_chunks, row_blocks;
+    int32_t chunk_tiles, max_chunks, row_blocks, waves;
     uint64_t pml_bytes, pacc_bytes, total;
 };
 
@@ -379,7 +379,13 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (total_q < 0 || max_q_len < 1) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / cache->num_kv_heads;
-    const int64_t rb = ((int64_t)max_q_len * group + 63) / 64;
+    // Waves per workgroup (16 query rows each): one when a sequence's rows fit
+    // a wave (speculative decoding: every wave then loads its own tiles and
+    // all workgroups fit on the chip at once), 4, or 16 so that up to 256 rows
+    // share each tile read.
+    const int64_t rows_max = (int64_t)max_q_len * group;
+    const int32_t waves = rows_max <= 16 ? 1 : rows_max <= 64 ? 4 : 16;
+    const int64_t rb = (rows_max + 16 * waves - 1) / (16 * waves);
     if (rb * cache->num_kv_heads > 65535 || (int64_t)max_q_len > 65535 || num_seqs > INT32_MAX - 1) return PKV_ERR_SHAPE;
     const int64_t tiles = ((int64_t)max_blocks_per_seq * cache->block_size + 15) / 16;
     int64_t ct;
@@ -395,6 +401,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     mp->chunk_tiles = (int32_t)ct;
     mp->max_chunks = (int32_t)mc;
     mp->row_blocks = (int32_t)rb;
+    mp->waves = waves;
     const uint64_t rows = (uint64_t)total_q * num_q_heads * (uint64_t)mc;
     mp->pml_bytes = align_up(rows * sizeof(float2), 256);
     mp->pacc_bytes = rows * (uint64_t)cache->head_dim * sizeof(float);
@@ -402,7 +409,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     mp->base.partition_tokens = (int32_t)ct * 16;
     mp->base.max_partitions = mp->max_chunks;
     mp->base.grid_blocks = (int64_t)num_seqs * cache->num_kv_heads * rb * mc;
-    mp->base.threads_per_block = 256;
+    mp->base.threads_per_block = 64 * waves;
     mp->base.workspace_bytes = mp->total;
     return PKV_OK;
 }
@@ -454,6 +461,7 @@ PKV_API pkv_status paged_attn_decode_multi(const void* q, const void* k_cache, c
     a.total_q = total_q;
     a.max_q_len = max_q_len;
     a.multi_row_blocks = mp.row_blocks;
+    a.multi_waves = mp.waves;
     a.prefix_chunk_tiles = mp.chunk_tiles;
     a.prefix_max_chunks = mp.max_chunks;
     a.ws_pml = reinterpret_cast<float2*>(ws);

@@ -941,14 +941,21 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
 }
 
 // Several new tokens per sequence, causal.  Workgroup (sequence i, KV head g
-// and block of 64 query rows, chunk c of the sequence's tiles) has four waves
-// and the tile pipeline of decode_prefix_kernel: each 16-token tile of the
-// chunk is read once into LDS for all of the sequence's new tokens.  Row r of
+// and block of 16 * MW query rows, chunk c of the sequence's tiles) has MW
+// waves of 16 rows and the tile pipeline of decode_prefix_kernel: each
+// 16-token tile of the chunk is read once into LDS, by all of the workgroup's
+// threads, for all of its rows.  MW is 1 when a sequence's rows fit one wave
+// (speculative decoding: no wave only loads, and the small workgroups all fit
+// on the chip at once), else 4 or 16 (up to 256 rows per tile read).  Row r of
 // a block is new token r / G (position ctx - q_len + r / G) and head r % G; a
 // row sees the tokens up to its own position (the others are masked in the
 // scores).  Each row leaves the chunk's (m, l, acc) for multi_merge_kernel.
-template <int BS, int G>
-__global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const DecodeArgs a, float qscale) {
+template <int BS, int G, int MW>
+__global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
+    constexpr int T = 64 * MW;        // threads: MW waves of 16 rows each
+    constexpr int TPI = 1024 / T;     // tokens of one dword column each thread moves per tile
+    constexpr int kAhead = MW == 1 ? 2 : 4;  // tiles in flight (32 / 8 / 2 load registers per tile)
+    static_assert(MW == 1 || MW == 4 || MW == 16, "waves per workgroup");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -967,13 +974,14 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
     // Sequences the merge reports as NaN, and blocks with no rows or tiles (uniform).
     if (q0 < 0 || q1 > a.total_q || ql < 1 || ql > a.max_q_len || ctx < ql || ctx > table_tokens) return;
     const int rows = ql * G;
-    if (64 * rb >= rows) return;
+    const int row0 = 16 * MW * rb;  // first row of this workgroup
+    if (row0 >= rows) return;
     const int nt_total = (ctx + kTok - 1) / kTok;
     const int t0 = c * CT;
     const int t1 = min(t0 + CT, nt_total);
     const int ntile = t1 - t0;
     if (ntile <= 0) return;
-    const bool computes = 64 * rb + 16 * wv < rows;
+    const bool computes = row0 + 16 * wv < rows;
 
     __shared__ uint2 toff_lds[kPrefixChunkTilesMax];
     __shared__ int tbad_lds[kPrefixChunkTilesMax];
@@ -992,7 +1000,7 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
     // This lane's row (for the scores and the softmax state): new token jq, head hq.
     const int r16 = lane & 15;
     const int grp = lane >> 4;
-    const int row = 64 * rb + 16 * wv + r16;
+    const int row = row0 + 16 * wv + r16;
     const bool real = row < rows;
     const int jq = real ? row / G : 0;
     const int pos = ctx - ql + jq;  // last token this row sees
@@ -1008,40 +1016,50 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
     }
     __syncthreads();
 
+    // Tile loads: thread (tg, vj) moves dword column vj (dims 2 vj, 2 vj + 1)
+    // of tokens tg * TPI .. + TPI - 1, of K and of V; each load instruction
+    // reads 256 contiguous bytes of one row.
     const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
     const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
-    const int vtg = tid >> 6, vj = tid & 63;
+    const int tg = tid >> 6, vj = tid & 63;
     struct TileKV {
-        uint4 k, v;
+        uint32_t k[TPI], v[TPI];
     };
-    auto load_tile = [&](int j) -> TileKV {
+    auto load_tile = [&](int j, TileKV& t) {
         const uint2 o = toff_lds[j];
-        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)(4 * vtg) * (kHd / 2) + vj;
-        TileKV t;
-        t.k = make_uint4(k32[off], k32[off + kHd / 2], k32[off + 2 * (kHd / 2)], k32[off + 3 * (kHd / 2)]);
-        t.v = make_uint4(v32[off], v32[off + kHd / 2], v32[off + 2 * (kHd / 2)], v32[off + 3 * (kHd / 2)]);
-        return t;
+        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)(TPI * tg) * (kHd / 2) + vj;
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) t.k[k] = k32[off + k * (kHd / 2)];
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) t.v[k] = v32[off + k * (kHd / 2)];
     };
-    // Value rows past the end of the context (the tail of the last tile) are
-    // stored as zeros: their weights are zero, and 0 * (whatever the slot
-    // holds, NaN included) must not reach the sums.  Key rows there only give
-    // scores that the mask replaces.
+    // K rows go to LDS as stored (padded rows); V goes transposed (one row
+    // per dim, 16 tokens).  Value rows past the end of the context (the tail
+    // of the last tile) are stored as zeros: their weights are zero, and
+    // 0 * (whatever the slot holds, NaN included) must not reach the sums.
+    // Key rows there only give scores that the mask replaces.
     auto store_tile = [&](int buf, const TileKV& t, int j) {
-        unsigned char* kb = &k_lds[buf][(4 * vtg) * kKRow + 4 * vj];
-        *reinterpret_cast<uint32_t*>(kb) = t.k.x;
-        *reinterpret_cast<uint32_t*>(kb + kKRow) = t.k.y;
-        *reinterpret_cast<uint32_t*>(kb + 2 * kKRow) = t.k.z;
-        *reinterpret_cast<uint32_t*>(kb + 3 * kKRow) = t.k.w;
-        const int tokb = (t0 + j) * kTok + 4 * vtg;
-        uint4 v = t.v;
-        v.x = tokb < ctx ? v.x : 0u;
-        v.y = tokb + 1 < ctx ? v.y : 0u;
-        v.z = tokb + 2 < ctx ? v.z : 0u;
-        v.w = tokb + 3 < ctx ? v.w : 0u;
-        const uint2 even = make_uint2((v.x & 0xffffu) | (v.y << 16), (v.z & 0xffffu) | (v.w << 16));
-        const uint2 odd = make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj) * kVtRow + 8 * vtg]) = even;
-        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj + 1) * kVtRow + 8 * vtg]) = odd;
+        unsigned char* kb = &k_lds[buf][(TPI * tg) * kKRow + 4 * vj];
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) *reinterpret_cast<uint32_t*>(kb + k * kKRow) = t.k[k];
+        const int tokb = (t0 + j) * kTok + TPI * tg;
+        uint32_t v[TPI];
+#pragma unroll
+        for (int k = 0; k < TPI; ++k) v[k] = tokb + k < ctx ? t.v[k] : 0u;
+        unsigned char* ve = &vt_lds[buf][(2 * vj) * kVtRow + 2 * TPI * tg];
+        unsigned char* vo = &vt_lds[buf][(2 * vj + 1) * kVtRow + 2 * TPI * tg];
+        if constexpr (TPI == 1) {
+            *reinterpret_cast<uint16_t*>(ve) = (uint16_t)(v[0] & 0xffffu);
+            *reinterpret_cast<uint16_t*>(vo) = (uint16_t)(v[0] >> 16);
+        } else {
+#pragma unroll
+            for (int k = 0; k < TPI; k += 4) {
+                const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
+                const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
+                *reinterpret_cast<uint2*>(ve + 2 * k) = even;
+                *reinterpret_cast<uint2*>(vo + 2 * k) = odd;
+            }
+        }
     };
 
     f32x4 acc[kHd / 16];
@@ -1101,22 +1119,26 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
         }
     };
 
-    TileKV R[kPrefixAhead];
+    // kAhead tiles in flight: every step issues one tile's loads (clamped to
+    // the last tile, so every path issues the same loads and each wait counts
+    // exactly the loads it needs), the loop runs in whole groups of kAhead and
+    // a tail finishes the last kAhead - 1 tiles.
+    TileKV R[kAhead];
 #pragma unroll
-    for (int q = 0; q < kPrefixAhead; ++q) R[q] = load_tile(min(q, ntile - 1));
+    for (int q = 0; q < kAhead; ++q) load_tile(min(q, ntile - 1), R[q]);
     int j0 = 0;
-    for (; j0 + kPrefixAhead <= ntile; j0 += kPrefixAhead) {
+    for (; j0 + kAhead <= ntile; j0 += kAhead) {
 #pragma unroll
-        for (int q = 0; q < kPrefixAhead; ++q) {
+        for (int q = 0; q < kAhead; ++q) {
             const int j = j0 + q;
             store_tile(j & 1, R[q], j);
-            R[q] = load_tile(min(j + kPrefixAhead, ntile - 1));
+            load_tile(min(j + kAhead, ntile - 1), R[q]);
             __syncthreads();
             if (computes) step(j & 1, j);
         }
     }
 #pragma unroll
-    for (int q = 0; q < kPrefixAhead - 1; ++q) {
+    for (int q = 0; q < kAhead - 1; ++q) {
         const int j = j0 + q;
         if (j < ntile) {  // uniform
             store_tile(j & 1, R[q], j);
@@ -1130,7 +1152,7 @@ __global__ __launch_bounds__(kPrefixThreads) void multi_query_kernel(const Decod
     const int MC = a.prefix_max_chunks;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-        const int r = 64 * rb + 16 * wv + 4 * grp + rr;
+        const int r = row0 + 16 * wv + 4 * grp + rr;
         if (r < rows) {
             const int64_t pr = ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + c;
 #pragma unroll
@@ -1221,7 +1243,12 @@ hipError_t launch_prefix_chunks(const DecodeArgs& a, hipStream_t stream) {
 template <int BS, int G>
 hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.num_seqs, (unsigned)(a.num_kv_heads * a.multi_row_blocks), (unsigned)a.prefix_max_chunks);
-    hipLaunchKernelGGL((multi_query_kernel<BS, G>), grid, dim3(kPrefixThreads), 0, stream, a, a.scale * kLog2e);
+    switch (a.multi_waves) {
+        case 1: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1>), grid, dim3(64), 0, stream, a, a.scale * kLog2e); break;
+        case 4: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4>), grid, dim3(256), 0, stream, a, a.scale * kLog2e); break;
+        case 16: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16>), grid, dim3(1024), 0, stream, a, a.scale * kLog2e); break;
+        default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid((unsigned)a.num_seqs, (unsigned)a.max_q_len, (unsigned)a.num_kv_heads);

@@ -45,7 +45,8 @@ struct DecodeArgs {
     const int32_t* cu_q;         // [S + 1] offsets of each sequence's query rows
     int32_t total_q;
     int32_t max_q_len;
-    int32_t multi_row_blocks;    // 64-row blocks per KV head
+    int32_t multi_row_blocks;    // row blocks (16 * multi_waves rows each) per KV head
+    int32_t multi_waves;         // waves per workgroup of the multi-query kernel: 1, 4 or 16
 };
 
 constexpr int32_t kMaxGridWaves = 8192;  // PKV_MAX_GRID_WAVES
