@@ -730,7 +730,12 @@ constexpr int kPrefixThreads = kPrefixWaves * 64;
 constexpr int kPrefixAhead = 4;           // tiles in flight per workgroup
 constexpr int kPrefixChunkTilesMax = 64;  // LDS table size
 constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes): conflict-free fragment reads
-constexpr int kVtRow = kTok * 2;          // LDS row of the transposed V tile (one dim, 16 tokens)
+// LDS row of the transposed V tile: one dim, 16 tokens (32 bytes), padded to
+// 40 bytes.  Rows 10 banks apart put the 16 rows that one P.V operand read
+// touches on 16 different bank pairs (conflict-free), and the tile's writes --
+// each lane its own dim row -- at most two to a bank; unpadded 32-byte rows
+// measured 75% of LDS cycles in bank conflicts.
+constexpr int kVtRow = kTok * 2 + 8;
 static_assert(kPrefixGroupMax * 8 <= 16 * kPrefixWaves, "rows of a full group at G = 8 fit the waves");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
