@@ -736,6 +736,12 @@ constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes):
 // each lane its own dim row -- at most two to a bank; unpadded 32-byte rows
 // measured 75% of LDS cycles in bank conflicts.
 constexpr int kVtRow = kTok * 2 + 8;
+// Byte offset of chunk c (tokens 4c .. 4c + 3) of transposed-V row (dim) d.
+// In rows 16 .. 31 of every 32 the chunks are swapped pairwise: the lanes that
+// write rows 2 vj and 2 vj + 16 then fall on different banks, while the 16
+// rows one operand read covers all share the swap, so that read stays
+// conflict-free.
+__device__ __forceinline__ int vt_off(int d, int c) { return d * kVtRow + 8 * (c ^ ((d >> 4) & 1)); }
 static_assert(kPrefixGroupMax * 8 <= 16 * kPrefixWaves, "rows of a full group at G = 8 fit the waves");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -823,8 +829,8 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
         const uint4 v = t.v;
         const uint2 even = make_uint2((v.x & 0xffffu) | (v.y << 16), (v.z & 0xffffu) | (v.w << 16));
         const uint2 odd = make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
-        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj) * kVtRow + 8 * vtg]) = even;
-        *reinterpret_cast<uint2*>(&vt_lds[buf][(2 * vj + 1) * kVtRow + 8 * vtg]) = odd;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][vt_off(2 * vj, vtg)]) = even;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][vt_off(2 * vj + 1, vtg)]) = odd;
     };
 
     f32x4 acc[kHd / 16];  // rows 4 grp .. + 3 of the wave, dims 16 jb + r16
@@ -874,7 +880,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
         }
 #pragma unroll
         for (int jb = 0; jb < kHd / 16; ++jb) {
-            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * jb + r16) * kVtRow + 8 * grp]);
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
             const s16x4 vv = __builtin_bit_cast(s16x4, vb);
             acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
             acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
@@ -1051,18 +1057,18 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
         uint32_t v[TPI];
 #pragma unroll
         for (int k = 0; k < TPI; ++k) v[k] = tokb + k < ctx ? t.v[k] : 0u;
-        unsigned char* ve = &vt_lds[buf][(2 * vj) * kVtRow + 2 * TPI * tg];
-        unsigned char* vo = &vt_lds[buf][(2 * vj + 1) * kVtRow + 2 * TPI * tg];
-        if constexpr (TPI == 1) {
-            *reinterpret_cast<uint16_t*>(ve) = (uint16_t)(v[0] & 0xffffu);
-            *reinterpret_cast<uint16_t*>(vo) = (uint16_t)(v[0] >> 16);
+        unsigned char* vb = &vt_lds[buf][0];
+        if constexpr (TPI == 1) {  // token tg: chunk tg / 4, position tg % 4
+            *reinterpret_cast<uint16_t*>(vb + vt_off(2 * vj, tg >> 2) + 2 * (tg & 3)) = (uint16_t)(v[0] & 0xffffu);
+            *reinterpret_cast<uint16_t*>(vb + vt_off(2 * vj + 1, tg >> 2) + 2 * (tg & 3)) = (uint16_t)(v[0] >> 16);
         } else {
 #pragma unroll
             for (int k = 0; k < TPI; k += 4) {
+                const int ch = (TPI * tg + k) >> 2;
                 const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
                 const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
-                *reinterpret_cast<uint2*>(ve + 2 * k) = even;
-                *reinterpret_cast<uint2*>(vo + 2 * k) = odd;
+                *reinterpret_cast<uint2*>(vb + vt_off(2 * vj, ch)) = even;
+                *reinterpret_cast<uint2*>(vb + vt_off(2 * vj + 1, ch)) = odd;
             }
         }
     };
@@ -1117,7 +1123,7 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
         }
 #pragma unroll
         for (int jb = 0; jb < kHd / 16; ++jb) {
-            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][(16 * jb + r16) * kVtRow + 8 * grp]);
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
             const s16x4 vv = __builtin_bit_cast(s16x4, vb);
             acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
             acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
