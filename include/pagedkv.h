@@ -83,7 +83,8 @@ typedef struct pkv_cache_desc {
 /* Kernel families of paged_attn_decode. */
 #define PKV_KERNEL_AUTO 0    /* library choice */
 #define PKV_KERNEL_GENERIC 1 /* any supported shape and dtype */
-#define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 16, 32 or 64, group size 1, 2, 4 or 8 */
+#define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 8, 16, 32 or 64, group size 1, 2, 4 or 8
+                                (block size 8: a 16-token tile reads two blocks) */
 
 /* Optional decode settings (host struct; NULL = all defaults). */
 typedef struct pkv_decode_opts {
@@ -198,9 +199,10 @@ pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_c
  * paged_attn_prefix_plan -- host-only plan of paged_attn_decode_prefix: the
  * fast kernel's plan with partition_tokens = tokens per prefix chunk,
  * max_partitions = chunks of the longest prefix, workspace_bytes = the
- * workspace paged_attn_decode_prefix needs.  Shapes as PKV_KERNEL_FAST
- * (PKV_ERR_UNSUPPORTED otherwise).  opts->partition_tokens, if nonzero, sets
- * the prefix chunk: a multiple of 16, at most 1024.
+ * workspace paged_attn_decode_prefix needs.  Shapes as PKV_KERNEL_FAST with
+ * block_size 16, 32 or 64 (PKV_ERR_UNSUPPORTED otherwise).
+ * opts->partition_tokens, if nonzero, sets the prefix chunk: a multiple of 16,
+ * at most 1024.
  */
 pkv_status paged_attn_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                   int32_t num_groups, int32_t max_prefix_tokens,
@@ -252,10 +254,12 @@ pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const vo
  * paged_attn_multi_plan -- host-only plan of paged_attn_decode_multi:
  * partition_tokens = tokens per context chunk, max_partitions = chunks of the
  * longest table, grid_blocks = workgroups of the chunk kernel,
- * workspace_bytes.  Shapes as PKV_KERNEL_FAST; max_q_len * (num_q_heads /
- * num_kv_heads) / 64 row blocks per KV head, at most 65535 in all.
- * opts->partition_tokens, if nonzero, sets the chunk (a multiple of 16, at
- * most 1024).
+ * workspace_bytes.  Shapes as PKV_KERNEL_FAST with block_size 16, 32 or 64
+ * (PKV_ERR_UNSUPPORTED otherwise).  The rows of a KV head, max_q_len *
+ * (num_q_heads / num_kv_heads), go to workgroups of 1, 4 or 16 waves of 16
+ * rows (the fewest that hold them, at most 16), in row blocks; at most 65535
+ * row blocks in all.  opts->partition_tokens, if nonzero, sets the chunk (a
+ * multiple of 16, at most 1024).
  */
 pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                                  int32_t max_blocks_per_seq, const pkv_cache_desc *cache,

@@ -257,6 +257,7 @@ pkv_status make_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_b
     o.kernel = PKV_KERNEL_FAST;
     pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &pp->base);
     if (st != PKV_OK) return st;
+    if (cache->block_size < 16) return PKV_ERR_UNSUPPORTED;  // the prefix pass reads whole 16-token tiles of one block
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (num_groups < 0 || max_prefix_tokens < 0) return PKV_ERR_SHAPE;
     if ((int64_t)max_prefix_tokens > (int64_t)max_blocks_per_seq * cache->block_size) return PKV_ERR_SHAPE;
@@ -376,6 +377,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     o.kernel = PKV_KERNEL_FAST;
     pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &mp->base);
     if (st != PKV_OK) return st;
+    if (cache->block_size < 16) return PKV_ERR_UNSUPPORTED;  // the chunk kernel reads whole 16-token tiles of one block
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (total_q < 0 || max_q_len < 1) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / cache->num_kv_heads;

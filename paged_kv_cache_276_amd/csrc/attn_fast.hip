@@ -1,5 +1,5 @@
 // attn_fast.hip -- paged decode attention for bf16 caches with head_dim 128
-// (block sizes 16, 32, 64; query-group sizes 1, 2, 4, 8) on gfx950.
+// (block sizes 8, 16, 32, 64; query-group sizes 1, 2, 4, 8) on gfx950.
 //
 // Work decomposition.  The unit of work is a tile: 16 consecutive logical
 // tokens of one (sequence, KV head).  All tiles are laid end to end in the
@@ -85,7 +85,8 @@ template <int BS, int G, bool START>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(const DecodeArgs a,
                                                                                                   float qscale) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-    static_assert(BS % kTok == 0, "block size");
+    static_assert(BS == 8 || BS % kTok == 0, "block size");
+    constexpr bool kSplit = BS < kTok;  // block size 8: a tile's rows 8..15 sit in the next block
     constexpr int ROWS = (G + 3) / 4;       // 16-lane rows that hold scores
     constexpr int kQv = (G * kHd * 2 + 1023) / 1024;  // 16-byte loads per lane for a unit's q rows
     constexpr int kSegRuns = G == 8 ? 4 : 8;          // runs (pieces of units) per segment
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             }
         }
         // tile records: lane j covers tiles j and j + 64 of the segment
-        int phys[2], trun[2];
+        int phys[2], phys2[2], trun[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int j = lane + kWave * half;
@@ -406,7 +407,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const int4 d = run_lds[r][0];
             const int4 e = run_lds[r][1];
             const int b = d.w + (j - e.z);
-            phys[half] = j < seg_len ? bt[(int64_t)d.x * maxB + (e.y + b * kTok) / BS] : 0;
+            const int tok0 = e.y + b * kTok;
+            phys[half] = j < seg_len ? bt[(int64_t)d.x * maxB + tok0 / BS] : 0;
+            // The second block of a split tile is looked up only when its half
+            // of the tile holds tokens (the entry past them may be unused).
+            phys2[half] = (kSplit && j < seg_len && tok0 + BS < e.w) ? bt[(int64_t)d.x * maxB + tok0 / BS + 1] : 0;
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -417,12 +422,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 const int4 e = run_lds[r][1];
                 const int b = d.w + (j - e.z);
                 const int tok0 = e.y + b * kTok;
-                const bool badp = (unsigned)phys[half] >= (unsigned)a.num_blocks;
+                bool badp = (unsigned)phys[half] >= (unsigned)a.num_blocks;
                 const int ph = badp ? 0 : phys[half];
                 const int64_t off = (((int64_t)ph * Hkv + d.y) * BS + (tok0 % BS)) * kHd;
+                // Split tile: (second block * Hkv + KV head) of rows 8..15; the
+                // first block again when that half holds no tokens, so that its
+                // (masked) key rows are still read from inside the pool.
+                uint32_t second = 0u;
+                if constexpr (kSplit) {
+                    int ph2 = ph;
+                    if (tok0 + BS < e.w) {
+                        const bool bad2 = (unsigned)phys2[half] >= (unsigned)a.num_blocks;
+                        badp = badp || bad2;
+                        ph2 = bad2 ? 0 : phys2[half];
+                    }
+                    second = (uint32_t)((int64_t)ph2 * Hkv + d.y);
+                }
                 const uint32_t flags = (uint32_t)min(kTok, e.w - tok0) | ((uint32_t)r << 8) |
                                        (b == 0 ? kFirst : 0u) | (b == d.z - 1 ? kLast : 0u) | (badp ? kBad : 0u);
-                rec_lds[j] = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), flags, 0u);
+                rec_lds[j] = make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), flags, second);
             }
         }
 #pragma unroll
@@ -448,12 +466,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const uint16_t* kt = kbase + tile_s;
             const uint16_t* vt = vbase + tile_s;
             const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
+            if constexpr (kSplit) {
+                // Rows BS.. of the tile live in the second block: they take
+                // `diff` more elements than rows of the first block would.
+                const int64_t tile2 = (int64_t)__builtin_amdgcn_readfirstlane(rv.w) * (BS * kHd);
+                const int64_t diff = tile2 - (tile_s + (int64_t)BS * kHd);
+                const int64_t kx = r16 >= BS ? diff : 0;
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
+                for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32 + kx);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
-                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int vr = min(4 * ii + grp, valid - 1);
+                    const int64_t voff = (int64_t)vr * kHd + r16 * 8 + (vr >= BS ? diff : 0);
+                    T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+                }
+            } else {
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
+                    T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+                }
             }
         };
 
@@ -1280,7 +1314,7 @@ hipError_t multi_by_group(const DecodeArgs& a, hipStream_t stream) {
 
 template <int BS, int G, bool PREFIX>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-    if (PREFIX) {
+    if constexpr (PREFIX) {
         const hipError_t e = launch_prefix_chunks<BS, G>(a, stream);
         if (e != hipSuccess) return e;
     }
@@ -1312,12 +1346,13 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
 
 bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
     const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
-    const bool b_ok = block_size == 16 || block_size == 32 || block_size == 64;
+    const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
     return dtype == 1 && head_dim == kHd && b_ok && g_ok;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
     switch (a.block_size) {
+        case 8: return by_group<8, false>(a, stream);
         case 16: return by_group<16, false>(a, stream);
         case 32: return by_group<32, false>(a, stream);
         case 64: return by_group<64, false>(a, stream);
