@@ -213,6 +213,26 @@ def test_bad_device_contents_stay_in_bounds():
             assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
 
 
+def test_block_size_8_tile_halves(oracle_impl):
+    """Block size 8: every 16-token tile of the fast kernel reads two blocks.  Lengths at and around
+    the half-tile and tile edges match the oracle; a table entry past a sequence's tokens is never
+    read, and a bad entry poisons exactly the sequences whose tokens use it."""
+    lens = [1, 7, 8, 9, 15, 16, 17, 24, 25, 100]
+    w = make_custom(lens, 8, 2, 128, 8, torch.bfloat16, seed=71, pool_fill=0.8)
+    assert pkv.PKV_KERNEL_FAST in _kernels_for(w)
+    for waves in (0, 3):
+        _check_step(w, oracle_impl, f"B8/waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
+    bad = make_custom([8, 9, 16, 40, 8], 8, 2, 128, 8, torch.bfloat16, seed=72, pool_fill=0.8)
+    bad.block_tables[0, 1] = bad.num_blocks + 5   # past sequence 0's 8 tokens: unused
+    bad.block_tables[1, 1] = bad.num_blocks + 5   # holds sequence 1's token 8
+    bad.block_tables[2, 1] = -3                   # holds sequence 2's tokens 8..15
+    bad.block_tables[4, 1:] = -1                  # past sequence 4's tokens
+    _, out = run_step(bad, kernel=pkv.PKV_KERNEL_FAST)
+    o = out.cpu()
+    assert torch.isfinite(o[0]).all() and torch.isfinite(o[3]).all() and torch.isfinite(o[4]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
+
+
 def test_write_bit_patterns():
     """Special bit patterns survive the append; skipped and out-of-range slots leave the pool untouched."""
     dev = torch.device("cuda", 0)
