@@ -1232,6 +1232,32 @@ __global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a,
         return;
     }
     const int64_t base = orow * a.prefix_max_chunks;
+    constexpr int kFew = 8;
+    if (nch <= kFew) {
+        // Lane p < nch holds chunk p's (m, l); every lane loads its two
+        // columns of all chunks at once.  Chunks the row cannot see (m = -inf)
+        // weigh nothing, whatever their l and acc hold.
+        const float2 mlv = lane < nch ? a.ws_pml[base + lane] : make_float2(-INFINITY, 0.f);
+        float2 v[kFew];
+#pragma unroll
+        for (int p = 0; p < kFew; ++p)
+            v[p] = p < nch ? *reinterpret_cast<const float2*>(a.ws_pacc + (base + p) * kHd + 2 * lane) : make_float2(0.f, 0.f);
+        const float M = read_lane(row_max16(mlv.x), 0);
+        const bool seen = lane < nch && mlv.x != -INFINITY;
+        const float wgt = seen ? exp2f(mlv.x - M) : 0.f;
+        const float L = read_lane(row_sum16(seen ? wgt * mlv.y : 0.f), 0);
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) {
+            const float wp = read_lane(wgt, p);
+            if (wp != 0.f) {  // uniform
+                o0 = fmaf(wp, v[p].x, o0);
+                o1 = fmaf(wp, v[p].y, o1);
+            }
+        }
+        *out = make_float2(o0 / L, o1 / L);
+        return;
+    }
     float M = -INFINITY;
     for (int p = lane; p < nch; p += kWave) M = fmaxf(M, a.ws_pml[base + p].x);
     M = wave_max(M);
