@@ -180,12 +180,14 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * Work splitting.  The generic kernel cuts every sequence into partitions of
  * plan.partition_tokens tokens and merges them in a second kernel.  The fast
  * kernel lays all (sequence, KV head, 16-token tile) triples end to end and
- * gives each wave of its grid an equal contiguous run of tiles, so a long
- * sequence spreads over several waves and many short ones share a wave; a
- * second kernel merges the pieces of each (sequence, KV head).
- * Either way every piece yields a running max, a softmax denominator and an
- * unnormalised output, merged by a log-sum-exp combine.  Results do not depend on the physical placement of blocks (the
- * summation order is fixed by logical token positions and the wave count).
+ * gives each wave of its grid a contiguous run of tiles (equal runs, or runs
+ * weighted by the wave's XCD: opts->xcd_balance), so a long sequence spreads
+ * over several waves and many short ones share a wave; a second kernel merges
+ * the pieces of each (sequence, KV head).  Either way every piece yields a
+ * running max, a softmax denominator and an unnormalised output, merged by a
+ * log-sum-exp combine.  Results do not depend on the physical placement of
+ * blocks (the summation order is fixed by logical token positions, the wave
+ * count and the XCD shares).
  * Calls that share a workspace must be serialised on one stream.
  */
 pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -361,7 +361,7 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
 namespace {
 
 // Several new tokens per sequence: chunks of the context per (sequence, KV
-// head, 64-row block) and the chunk partials.
+// head, row block of 16 * waves rows) and the chunk partials.
 struct MultiPlan {
     pkv_decode_plan base;
     int32_t chunk_tiles, max_chunks, row_blocks, waves;
