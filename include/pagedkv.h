@@ -262,6 +262,12 @@ pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const vo
  * rows (the fewest that hold them, at most 16), in row blocks; at most 65535
  * row blocks in all.  opts->partition_tokens, if nonzero, sets the chunk (a
  * multiple of 16, at most 1024).
+ * With one wave per row block (max_q_len * G <= 16) and no chunk asked for,
+ * the 16-token tiles of all (sequence, KV head) pairs are instead split in
+ * equal runs over opts->grid_waves waves (0: the waves the device keeps
+ * resident): partition_tokens = 16, max_partitions = PKV_MAX_GRID_WAVES,
+ * grid_blocks = opts->grid_waves, and the workspace holds one record per
+ * (sequence, KV head) and partial slots of 16 rows.
  */
 pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                                  int32_t max_blocks_per_seq, const pkv_cache_desc *cache,
@@ -290,10 +296,13 @@ pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_
  * Everything else as paged_attn_decode; the workspace is
  * paged_attn_multi_plan's (no initialisation needed).
  *
- * Device contents are not validated on the host.  A sequence with q_len < 1,
+ * Device contents are not validated on the host.  A sequence with
  * q_len > max_q_len or > context_lens[i], or a length past the table, gets NaN
- * rows (for its first max_q_len tokens); offsets outside [0, total_q] leave
- * that sequence's rows unwritten.  The kernels stay inside their buffers.
+ * rows (for its first max_q_len tokens); q_len < 1 or offsets outside
+ * [0, total_q] leave that sequence's rows unwritten.  A block-table entry
+ * outside the pool among the blocks a (sequence, KV head) reads gives NaN
+ * rows: all of its rows on the split runs, the rows that see the entry's
+ * chunk with chunks.  The kernels stay inside their buffers.
  */
 pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const void *v_cache,
                                    const int32_t *block_tables, int32_t max_blocks_per_seq,

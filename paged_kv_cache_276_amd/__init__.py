@@ -291,12 +291,17 @@ def paged_attn_decode_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
 
 
 def paged_attn_multi_plan(num_seqs: int, total_q: int, max_q_len: int, num_q_heads: int, max_blocks_per_seq: int,
-                          cache, chunk_tokens: int = 0) -> Dict[str, int]:
-    """Host-only plan of the multi-token attention (context chunk, chunks, workgroups, workspace bytes)."""
+                          cache, chunk_tokens: int = 0, grid_waves: int = 0) -> Dict[str, int]:
+    """Host-only plan of the multi-token attention (context chunk, chunks, workgroups, workspace bytes).
+
+    With one wave per row block (max_q_len * G <= 16) and chunk_tokens 0 the tiles are split in equal runs
+    over the resident waves (or grid_waves waves): chunk_tokens is then 16 and workgroups the wave count
+    asked for (0 = the device's resident waves)."""
     desc = cache if isinstance(cache, CacheDesc) else cache_desc(cache)
     plan = DecodePlan()
     st = _lib.lib().paged_attn_multi_plan(num_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq,
-                                          ctypes.byref(desc), ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, 0)),
+                                          ctypes.byref(desc),
+                                          ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)),
                                           ctypes.byref(plan))
     _lib.check(st, "paged_attn_multi_plan")
     return {"chunk_tokens": plan.partition_tokens, "max_chunks": plan.max_partitions,
@@ -307,7 +312,7 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                             block_tables: torch.Tensor, context_lens: torch.Tensor, cu_q_lens: torch.Tensor,
                             max_q_len: int, scale: float, out: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None, chunk_tokens: int = 0,
-                            stream=None) -> torch.Tensor:
+                            grid_waves: int = 0, stream=None) -> torch.Tensor:
     """Causal attention of several new tokens per sequence over the paged cache (fp32 out [total_q][Hq][D])."""
     dev = k_cache.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
@@ -328,7 +333,7 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     _dev(out, "out", dev)
     _need(out.dtype == torch.float32 and tuple(out.shape) == (TQ, Hq, desc.head_dim), "out must be fp32 [total_q][Hq][D]")
     maxb = block_tables.shape[1]
-    plan = paged_attn_multi_plan(S, TQ, max_q_len, Hq, maxb, desc, chunk_tokens)
+    plan = paged_attn_multi_plan(S, TQ, max_q_len, Hq, maxb, desc, chunk_tokens, grid_waves)
     s = _stream(dev, stream)
     need = plan["workspace_bytes"]
     if workspace is None:
@@ -342,6 +347,6 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         ctypes.c_void_p(cu_q_lens.data_ptr()), S, TQ, int(max_q_len), Hq, ctypes.c_float(scale),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), ctypes.byref(desc),
-        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, 0)), s)
+        ctypes.byref(_opts(chunk_tokens, PKV_KERNEL_AUTO, grid_waves)), s)
     _lib.check(st, "paged_attn_decode_multi")
     return out

@@ -362,10 +362,15 @@ namespace {
 
 // Several new tokens per sequence: chunks of the context per (sequence, KV
 // head, row block of 16 * waves rows) and the chunk partials.
+// With one wave per row block and no chunk asked for, the tiles are split in
+// equal runs over the resident waves instead (partials per slot unit + wave,
+// 16 rows each, after one record per unit, as in fast_layout).
 struct MultiPlan {
     pkv_decode_plan base;
     int32_t chunk_tiles, max_chunks, row_blocks, waves;
+    bool split_runs;
     uint64_t pml_bytes, pacc_bytes, total;
+    WorkspaceLayout runs;
 };
 
 pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
@@ -389,6 +394,28 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     const int32_t waves = rows_max <= 16 ? 1 : rows_max <= 64 ? 4 : 16;
     const int64_t rb = (rows_max + 16 * waves - 1) / (16 * waves);
     if (rb * cache->num_kv_heads > 65535 || (int64_t)max_q_len > 65535 || num_seqs > INT32_MAX - 1) return PKV_ERR_SHAPE;
+    mp->waves = waves;
+    mp->row_blocks = (int32_t)rb;
+    mp->split_runs = waves == 1 && chunk_tokens == 0;
+    if (mp->split_runs) {
+        const uint64_t units = (uint64_t)num_seqs * (uint64_t)cache->num_kv_heads;
+        const uint64_t slots = units + (uint64_t)pkv::kMaxGridWaves;
+        WorkspaceLayout& w = mp->runs;
+        w.rec_bytes = align_up(units * sizeof(int2), 256);
+        w.ml_bytes = align_up(slots * 16 * sizeof(float2), 256);
+        w.acc_bytes = slots * 16 * (uint64_t)cache->head_dim * sizeof(float);
+        w.total = w.rec_bytes + w.ml_bytes + w.acc_bytes;
+        mp->chunk_tiles = 0;
+        mp->max_chunks = 0;
+        mp->pml_bytes = mp->pacc_bytes = 0;
+        mp->total = w.total;
+        mp->base.partition_tokens = 16;
+        mp->base.max_partitions = pkv::kMaxGridWaves;
+        mp->base.grid_blocks = opts ? opts->grid_waves : 0;
+        mp->base.threads_per_block = 64;
+        mp->base.workspace_bytes = mp->total;
+        return PKV_OK;
+    }
     const int64_t tiles = ((int64_t)max_blocks_per_seq * cache->block_size + 15) / 16;
     int64_t ct;
     if (chunk_tokens) {
@@ -402,8 +429,6 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     if (mc > 65535) return PKV_ERR_SHAPE;
     mp->chunk_tiles = (int32_t)ct;
     mp->max_chunks = (int32_t)mc;
-    mp->row_blocks = (int32_t)rb;
-    mp->waves = waves;
     const uint64_t rows = (uint64_t)total_q * num_q_heads * (uint64_t)mc;
     mp->pml_bytes = align_up(rows * sizeof(float2), 256);
     mp->pacc_bytes = rows * (uint64_t)cache->head_dim * sizeof(float);
@@ -466,8 +491,16 @@ PKV_API pkv_status paged_attn_decode_multi(const void* q, const void* k_cache, c
     a.multi_waves = mp.waves;
     a.prefix_chunk_tiles = mp.chunk_tiles;
     a.prefix_max_chunks = mp.max_chunks;
-    a.ws_pml = reinterpret_cast<float2*>(ws);
-    a.ws_pacc = reinterpret_cast<float*>(ws + mp.pml_bytes);
+    a.multi_split_runs = mp.split_runs ? 1 : 0;
+    if (mp.split_runs) {
+        a.ws_rec = reinterpret_cast<int2*>(ws);
+        a.ws_ml = reinterpret_cast<float2*>(ws + mp.runs.rec_bytes);
+        a.ws_acc = reinterpret_cast<float*>(ws + mp.runs.rec_bytes + mp.runs.ml_bytes);
+        a.grid_waves = opts ? opts->grid_waves : 0;
+    } else {
+        a.ws_pml = reinterpret_cast<float2*>(ws);
+        a.ws_pacc = reinterpret_cast<float*>(ws + mp.pml_bytes);
+    }
     const hipError_t e = pkv::launch_decode_multi(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

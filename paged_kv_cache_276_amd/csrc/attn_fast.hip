@@ -1279,6 +1279,380 @@ __global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a,
     *out = make_float2(o0 / L, o1 / L);
 }
 
+// Several new tokens per sequence with all of a KV head's rows in one 16-row
+// block (q_len * G <= 16: the verification of a few drafted tokens).  The
+// tiles of all (sequence, KV head) units are laid end to end, as in
+// decode_fast_kernel, and split into equal runs over the resident waves, so a
+// wave's share does not depend on the length mix.  A wave walks its run in
+// pieces of one unit each; a piece goes through LDS in segments of up to
+// kPrefixChunkTilesMax tiles with the tile pipeline of multi_query_kernel (K as
+// stored, V transposed, q.K and P.V on the matrix cores).  At the end of a
+// piece the wave writes the unit's output rows (it saw all of the unit's tiles)
+// or each row's (m, l, acc) to partial slot unit + wave; the wave holding the
+// unit's first tile records the first slot and the number of partials (waves
+// from it to the one holding the unit's last tile) for multi_sk_merge_kernel.
+template <int BS, int G>
+__global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float qscale) {
+    constexpr int kAhead = 3;  // tiles in flight (32 load registers each; 3 measured 3% faster than 2)
+    constexpr int kSegMax = kPrefixChunkTilesMax;
+    const int lane = threadIdx.x;
+    const int nwaves = gridDim.x;
+    const int bid = blockIdx.x;
+    const int w = (nwaves % 8 == 0) ? (bid % 8) * (nwaves / 8) + bid / 8 : bid;
+    const int S = a.num_seqs, Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int maxB = a.max_blocks_per_seq;
+    const int table_tokens = maxB * BS;
+
+    // Tiles of sequence i < S; none for a description the merge reports as NaN
+    // rows or leaves unwritten.
+    auto seq_tiles = [&](int i) -> int {
+        const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1], ctx = a.context_lens[i];
+        const int64_t ql = (int64_t)q1 - q0;
+        const bool ok = q0 >= 0 && q1 <= a.total_q && ql >= 1 && ql <= a.max_q_len && ctx >= ql && ctx <= table_tokens;
+        return ok ? (ctx + kTok - 1) / kTok : 0;
+    };
+
+    // ---- total tiles, one sequence per lane and round
+    int total = 0;
+    for (int base = 0; base < S; base += kWave) {
+        const int i = base + lane;
+        const int n = seq_tiles(min(i, S - 1));
+        total += wave_sum_int(i < S ? n : 0);
+    }
+    const int64_t Nt = (int64_t)total * Hkv;
+    if (Nt == 0) return;
+    const int W = (int)min<int64_t>(Nt, nwaves);
+    if (w >= W) return;
+    const Split sp = make_split(Nt, W, nwaves, 64);  // equal runs, every wave at least one tile
+    const int64_t c0 = sp.start(w), c1 = sp.start(w + 1);
+
+    // ---- the sequence holding tile c0, and its first tile's global index
+    int i = -1;
+    int64_t seq_base = 0;
+    {
+        int64_t acc = 0;
+        for (int base = 0; base < S; base += kWave) {
+            const int il = base + lane;
+            const int nl = seq_tiles(min(il, S - 1));
+            const int n = il < S ? nl : 0;
+            const int incl = wave_incl_scan_int(n);
+            const int64_t chunk = (int64_t)read_lane(incl, kWave - 1) * Hkv;
+            if (c0 < acc + chunk) {
+                const int L = __ffsll(__ballot(acc + (int64_t)incl * Hkv > c0)) - 1;
+                i = base + L;
+                seq_base = acc + (int64_t)read_lane(incl - n, L) * Hkv;
+                break;
+            }
+            acc += chunk;
+        }
+    }
+    if (i < 0) return;  // unreachable when the two passes agree
+    int n = seq_tiles(i);
+    int g, b;
+    {
+        const int64_t off = c0 - seq_base;  // < n * Hkv
+        g = (int)(off / n);
+        b = (int)(off - (int64_t)g * n);
+    }
+
+    __shared__ uint2 toff_lds[kSegMax];
+    __shared__ int tbad_lds[kSegMax];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
+    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][kHd * kVtRow];
+
+    const int32_t* __restrict__ bt = a.block_tables;
+    const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
+    const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
+    const int r16 = lane & 15;  // this lane's row (scores, softmax state) / output column
+    const int grp = lane >> 4;
+    // Tile loads: lane l moves dword column l (dims 2l, 2l + 1) of all 16
+    // tokens of K and of V; each load instruction reads one 256-byte row.
+    struct TileKV {
+        uint32_t k[kTok], v[kTok];
+    };
+
+    for (int64_t t = c0; t < c1;) {
+        const int len = (int)min<int64_t>((int64_t)(n - b), c1 - t);  // tiles of this piece
+        const int q0 = a.cu_q[i];
+        const int ql = a.cu_q[i + 1] - q0;
+        const int ctx = a.context_lens[i];
+        const int rows = ql * G;
+        const bool real = r16 < rows;
+        const int jq = real ? r16 / G : 0;
+        const int pos = ctx - ql + jq;  // last token row r16 sees
+        uint4 qc[4];
+        {
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                                   ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? r16 % G : 0)) * kHd;
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
+                qc[kq] = real ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
+        f32x4 acc[kHd / 16];
+#pragma unroll
+        for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY;
+        float l = 0.f;
+        bool bad = false;
+
+        for (int t0 = b; t0 < b + len; t0 += kSegMax) {  // tiles t0 .. t0 + ntile - 1 of the unit
+            const int ntile = min(kSegMax, b + len - t0);
+            if (lane < ntile) {
+                const int tok0 = (t0 + lane) * kTok;
+                const int phys = bt[(int64_t)i * maxB + tok0 / BS];
+                const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
+                const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * kHd;
+                toff_lds[lane] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
+                tbad_lds[lane] = badp;
+            }
+            __syncthreads();
+
+            auto load_tile = [&](int j, TileKV& tk) {
+                const uint2 o = toff_lds[j];
+                const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
+#pragma unroll
+                for (int k = 0; k < kTok; ++k) tk.k[k] = k32[off + k * (kHd / 2)];
+#pragma unroll
+                for (int k = 0; k < kTok; ++k) tk.v[k] = v32[off + k * (kHd / 2)];
+            };
+            // K rows as stored (padded rows); V transposed, its rows past the
+            // context stored as zeros (0 * whatever the slot holds must not
+            // reach the sums; the key rows there only give masked scores).
+            auto store_tile = [&](int buf, const TileKV& tk, int j) {
+                unsigned char* kb = &k_lds[buf][4 * lane];
+#pragma unroll
+                for (int k = 0; k < kTok; ++k) *reinterpret_cast<uint32_t*>(kb + k * kKRow) = tk.k[k];
+                const int tokb = (t0 + j) * kTok;
+                uint32_t v[kTok];
+#pragma unroll
+                for (int k = 0; k < kTok; ++k) v[k] = tokb + k < ctx ? tk.v[k] : 0u;
+                unsigned char* vb = &vt_lds[buf][0];
+#pragma unroll
+                for (int k = 0; k < kTok; k += 4) {
+                    const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
+                    const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
+                    *reinterpret_cast<uint2*>(vb + vt_off(2 * lane, k >> 2)) = even;
+                    *reinterpret_cast<uint2*>(vb + vt_off(2 * lane + 1, k >> 2)) = odd;
+                }
+            };
+            auto step = [&](int buf, int j) {
+                bad = bad || tbad_lds[j] != 0;
+                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) {
+                    const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qc[kq]), sc, 0, 0, 0);
+                }
+                const int tok = (t0 + j) * kTok + 4 * grp;
+                float s[4];
+                bool vis[4];
+                bool need = false;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vis[r] = real && tok + r <= pos;
+                    s[r] = vis[r] ? sc[r] * qscale : -INFINITY;
+                    need = need || (vis[r] && s[r] > m + kLazyRescale);
+                }
+                if (__any(need)) {
+                    float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                    tm = max_xor32(max_xor16(tm));
+                    const float mn = tm > m + kLazyRescale ? tm : m;
+                    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
+                    m = mn;
+                    l *= alpha;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float ar = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+                        for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
+                    }
+                }
+                s16x4 phi, plo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = vis[r] ? fast_exp2(s[r] - m) : 0.f;
+                    l += pr;
+                    const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
+                    phi[r] = (short)(hb >> 16);
+                    plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
+                }
+#pragma unroll
+                for (int jb = 0; jb < kHd / 16; ++jb) {
+                    const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
+                    const s16x4 vv = __builtin_bit_cast(s16x4, vb);
+                    acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
+                    acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
+                }
+            };
+
+            // The pipeline of multi_query_kernel: every step issues one tile's
+            // loads (clamped to the segment's last tile), whole groups of
+            // kAhead, then the last kAhead - 1 tiles.
+            TileKV R[kAhead];
+#pragma unroll
+            for (int q = 0; q < kAhead; ++q) load_tile(min(q, ntile - 1), R[q]);
+            int j0 = 0;
+            for (; j0 + kAhead <= ntile; j0 += kAhead) {
+#pragma unroll
+                for (int q = 0; q < kAhead; ++q) {
+                    const int j = j0 + q;
+                    store_tile(j & 1, R[q], j);
+                    load_tile(min(j + kAhead, ntile - 1), R[q]);
+                    __syncthreads();
+                    step(j & 1, j);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kAhead - 1; ++q) {
+                const int j = j0 + q;
+                if (j < ntile) {  // uniform
+                    store_tile(j & 1, R[q], j);
+                    __syncthreads();
+                    step(j & 1, j);
+                }
+            }
+            __syncthreads();  // the next segment rewrites the tables and tiles
+        }
+
+        // ---- end of the piece: lane (r16, grp) holds rows 4 grp .. 4 grp + 3,
+        // column r16 of every 16-dim block; row r's l is in lane r.
+        const float lt = sum_xor32(sum_xor16(l));
+        const int64_t u = (int64_t)i * Hkv + g;
+        const int64_t slot = u + w;
+        const bool whole = b == 0 && len == n;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 4 * grp + rr;
+            const float lr = __shfl(lt, r, kWave);
+            if (r < rows) {
+                if (whole) {
+                    float* o = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+                    const float inv = bad ? NAN : 1.f / lr;
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) o[16 * jb + r16] = acc[jb][rr] * inv;
+                } else {
+                    float* o = a.ws_acc + (slot * 16 + r) * kHd;
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) o[16 * jb + r16] = acc[jb][rr];
+                }
+            }
+        }
+        if (!whole && lane < 16 && real) a.ws_ml[slot * 16 + r16] = make_float2(m, bad ? NAN : lt);
+        if (b == 0 && lane == 0) {
+            const int64_t last_tile = seq_base + (int64_t)g * n + n - 1;
+            const int rcount = whole ? 1 : (int)(sp.wave_of(last_tile) - w + 1);
+            a.ws_rec[u] = make_int2((int)slot, rcount);
+        }
+
+        // ---- next piece
+        t += len;
+        b += len;
+        if (b == n && t < c1) {
+            b = 0;
+            if (++g == Hkv) {
+                g = 0;
+                seq_base += (int64_t)Hkv * n;
+                do {
+                    ++i;
+                } while (i < S && seq_tiles(i) == 0);
+                if (i >= S) return;  // unreachable when the two passes agree
+                n = seq_tiles(i);
+            }
+        }
+    }
+}
+
+// Merge for multi_sk_kernel: one workgroup per (sequence, new token j, KV
+// head g), one wave per query head h of the group, lanes owning two columns.
+// Units the tile kernel finished (one partial) are left alone; otherwise row
+// r = j * G + h of the unit gets out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p
+// - M) l_p over the unit's partial slots in order (a partial whose tiles all
+// lie past the row's position has m = -inf and weighs nothing).  Invalid
+// sequence descriptions give NaN rows.
+template <int G>
+__global__ __launch_bounds__(64 * G) void multi_sk_merge_kernel(const DecodeArgs a, int table_tokens) {
+    constexpr int kFew = 8;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int h = threadIdx.x / kWave;
+    const int i = blockIdx.x, j = blockIdx.y, g = blockIdx.z;
+    const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
+    const int ctx = a.context_lens[i];
+    const int64_t u = (int64_t)i * a.num_kv_heads + g;
+    const int2 rec = a.ws_rec[u];  // garbage, and unused, for an invalid sequence
+    const int64_t ql = (int64_t)q1 - q0;
+    if (q0 < 0 || q1 > a.total_q || ql < 1 || j >= ql) return;  // no row to write
+    float2* out = reinterpret_cast<float2*>(
+        a.out + ((int64_t)(q0 + j) * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
+    if (ql > a.max_q_len || ctx < ql || ctx > table_tokens) {
+        *out = make_float2(NAN, NAN);
+        return;
+    }
+    if (rec.y == 1) return;  // finished by the tile kernel
+    const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
+    if (rec.y < 1 || rec.x < 0 || (int64_t)rec.x + rec.y > slots) {  // never written: refuse to read
+        *out = make_float2(NAN, NAN);
+        return;
+    }
+    const int np = rec.y;
+    const int r = j * G + h;  // < max_q_len * G <= 16
+    auto ml_of = [&](int p) -> float2 { return a.ws_ml[((int64_t)rec.x + p) * 16 + r]; };
+    auto acc_of = [&](int p) -> float2 {
+        return *reinterpret_cast<const float2*>(a.ws_acc + (((int64_t)rec.x + p) * 16 + r) * kHd + 2 * lane);
+    };
+    if (np <= kFew) {
+        const float2 mlv = lane < np ? ml_of(lane) : make_float2(-INFINITY, 0.f);
+        float2 v[kFew];
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) v[p] = p < np ? acc_of(p) : make_float2(0.f, 0.f);
+        const float M = wave_max(mlv.x);
+        const float wgt = lane < np ? exp2f(mlv.x - M) : 0.f;
+        const float L = wave_sum(wgt * mlv.y);
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int p = 0; p < kFew; ++p) {
+            const float wp = read_lane(wgt, p);
+            o0 = fmaf(wp, v[p].x, o0);
+            o1 = fmaf(wp, v[p].y, o1);
+        }
+        *out = make_float2(o0 / L, o1 / L);
+        return;
+    }
+    float M = -INFINITY;
+    for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml_of(p).x);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int p = lane; p < np; p += kWave) {
+        const float2 v = ml_of(p);
+        L += exp2f(v.x - M) * v.y;
+    }
+    L = wave_sum(L);
+    float o0 = 0.f, o1 = 0.f;
+    int p = 0;
+    for (; p + 4 <= np; p += 4) {  // four partials' loads in flight at once
+        float2 v[4], mlv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = acc_of(p + k);
+            mlv[k] = ml_of(p + k);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float wgt = exp2f(mlv[k].x - M);
+            o0 = fmaf(wgt, v[k].x, o0);
+            o1 = fmaf(wgt, v[k].y, o1);
+        }
+    }
+    for (; p < np; ++p) {
+        const float2 v = acc_of(p);
+        const float wgt = exp2f(ml_of(p).x - M);
+        o0 = fmaf(wgt, v.x, o0);
+        o1 = fmaf(wgt, v.y, o1);
+    }
+    *out = make_float2(o0 / L, o1 / L);
+}
+
 namespace {
 
 // Resident waves of one kernel on the current device (cached).
@@ -1313,6 +1687,17 @@ hipError_t launch_prefix_chunks(const DecodeArgs& a, hipStream_t stream) {
 
 template <int BS, int G>
 hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
+    const dim3 mgrid((unsigned)a.num_seqs, (unsigned)a.max_q_len, (unsigned)a.num_kv_heads);
+    if (a.multi_split_runs) {
+        const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, G>);
+        const int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
+        if (waves <= 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((multi_sk_kernel<BS, G>), dim3(waves), dim3(kWave), 0, stream, a, a.scale * kLog2e);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((multi_sk_merge_kernel<G>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)a.num_seqs, (unsigned)(a.num_kv_heads * a.multi_row_blocks), (unsigned)a.prefix_max_chunks);
     switch (a.multi_waves) {
         case 1: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1>), grid, dim3(64), 0, stream, a, a.scale * kLog2e); break;
@@ -1322,7 +1707,6 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid((unsigned)a.num_seqs, (unsigned)a.max_q_len, (unsigned)a.num_kv_heads);
     hipLaunchKernelGGL((multi_merge_kernel<G>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
     return hipGetLastError();
 }

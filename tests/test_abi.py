@@ -127,6 +127,31 @@ def test_prefix_and_multi_plans_need_whole_tiles(L):
         assert st == expect, (b, st)
 
 
+def test_multi_plan_split_runs(L):
+    """One wave per row block (max_q_len * G <= 16) and no chunk asked for: equal runs of 16-token
+    tiles over the waves (workgroups = the wave count asked for, 0 = the device's), partials per slot
+    unit + wave of 16 rows after one record per unit.  A chunk asked for, or more rows, keeps chunks."""
+    from paged_kv_cache_276_amd import DecodeOpts, DecodePlan
+
+    def mplan(max_q_len, chunk=0, waves=0, hq=32):
+        plan = DecodePlan()
+        st = L.paged_attn_multi_plan(64, 64 * max_q_len, max_q_len, hq, 256, ctypes.byref(_desc(nb=30000)),
+                                     ctypes.byref(DecodeOpts(chunk, 0, waves, 0)), ctypes.byref(plan))
+        return st, plan
+
+    units, slots = 64 * 8, 64 * 8 + 8192
+    for waves in (0, 8, 100):
+        st, plan = mplan(4, waves=waves)
+        assert st == 0 and plan.partition_tokens == 16 and plan.grid_blocks == waves
+        assert plan.threads_per_block == 64
+        assert plan.workspace_bytes >= units * 8 + slots * 16 * (128 * 4 + 8)
+    st, plan = mplan(4, chunk=256)
+    assert st == 0 and plan.partition_tokens == 256 and plan.threads_per_block == 64
+    st, plan = mplan(5)  # 20 rows: four waves per workgroup, chunks
+    assert st == 0 and plan.threads_per_block == 256 and plan.partition_tokens != 16
+    assert mplan(4, waves=8193)[0] == 2
+
+
 def test_plan_xcd_balance(L):
     """The odd-XCD share is 1..127 in 64ths (0 = library choice); anything else is refused, and the
     library's default is the header's PKV_XCD_BALANCE_DEFAULT, mirrored in the binding."""

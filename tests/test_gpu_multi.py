@@ -18,15 +18,16 @@ from workloads import MULTI_CONFIG_NAMES, make_multi, make_multi_config
 pytestmark = pytest.mark.gpu
 
 
-def run_multi(w, chunk_tokens=0, cu_override=None, max_q_len=None):
+def run_multi(w, chunk_tokens=0, cu_override=None, max_q_len=None, grid_waves=0, tables=None):
     dev = device()
     kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
     pkv.paged_kv_write(w.k_new.to(dev), w.v_new.to(dev), torch.from_numpy(w.slot_mapping).to(dev), kc, vc)
     cu = w.cu_q if cu_override is None else np.asarray(cu_override, dtype=np.int32)
     mq = max_q_len or int(np.max(np.diff(w.cu_q)))
-    out = pkv.paged_attn_decode_multi(w.q.to(dev), kc, vc, torch.from_numpy(w.block_tables).to(dev),
+    bt = w.block_tables if tables is None else tables
+    out = pkv.paged_attn_decode_multi(w.q.to(dev), kc, vc, torch.from_numpy(bt).to(dev),
                                       torch.from_numpy(w.context_lens).to(dev), torch.from_numpy(cu).to(dev),
-                                      mq, w.scale, chunk_tokens=chunk_tokens)
+                                      mq, w.scale, chunk_tokens=chunk_tokens, grid_waves=grid_waves)
     torch.cuda.synchronize()
     return kc, vc, out
 
@@ -38,10 +39,10 @@ def reference(w, oracle_impl):
     return kc, vc, out
 
 
-def _check(w, oracle_impl, what, chunk_tokens=0):
+def _check(w, oracle_impl, what, chunk_tokens=0, grid_waves=0):
     say(f"[gpu] multi {what}: S={w.num_seqs} total_q={int(w.cu_q[-1])} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
-        f"B={w.block_size} chunk={chunk_tokens}")
-    kc, vc, out = run_multi(w, chunk_tokens)
+        f"B={w.block_size} chunk={chunk_tokens} waves={grid_waves}")
+    kc, vc, out = run_multi(w, chunk_tokens, grid_waves=grid_waves)
     rk, rv, ref = reference(w, oracle_impl)
     assert np.array_equal(bits(kc), rk) and np.array_equal(bits(vc), rv), f"{what}: pools differ after the write"
     ratio = assert_parity(out, ref, what)
@@ -112,3 +113,57 @@ def test_malformed_sequences_give_nan_rows():
     _, _, out = run_multi(w, cu_override=cu, max_q_len=4)
     assert torch.isnan(out[4:8]).all()
     assert torch.equal(out[:4], good[:4])
+
+
+# Split runs (one wave per row block, no chunk asked for): the tiles of all (sequence, KV head) units are
+# dealt in equal runs to the waves.  Few waves give pieces longer than one 64-tile LDS table and units
+# with more than 8 partials (the merge's second path); a wave count that is not a multiple of 8 uses the
+# plain wave order.
+SPLIT_CASES = [
+    # lengths, q_lens, Hq, Hkv, B
+    ([1, 3, 15, 16, 17, 100, 1000, 2049], [1, 3, 2, 4, 4, 1, 4, 3], 8, 2, 16),     # G = 4, q_len = ctx
+    ([4096, 50, 700], [16, 7, 16], 2, 2, 32),                                    # G = 1, 16 rows
+    ([333, 2000, 64, 65], [2, 1, 2, 2], 16, 2, 64),                                # G = 8
+    ([5000, 31, 800, 1], [8, 8, 5, 1], 8, 4, 16),                                 # G = 2
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_multi_split_runs(case, oracle_impl):
+    lengths, qls, hq, hkv, B = SPLIT_CASES[case]
+    w = make_multi(lengths, qls, hq, hkv, 128, B, torch.bfloat16, seed=300 + case, pool_fill=0.8)
+    plan = pkv.paged_attn_multi_plan(w.num_seqs, int(w.cu_q[-1]), int(max(qls)), hq, w.block_tables.shape[1],
+                                     pkv.cache_desc(w.k_cache), 0, 24)
+    assert plan["chunk_tokens"] == 16 and plan["workgroups"] == 24, plan
+    outs = []
+    for gw in (0, 3, 8, 24, 64, 1000):
+        out, ref = _check(w, oracle_impl, f"split{case}/w{gw}", grid_waves=gw)
+        outs.append(out)
+    chunked, _ = _check(w, oracle_impl, f"split{case}/ct64", chunk_tokens=64)
+    assert torch.allclose(outs[0], chunked, atol=2e-3, rtol=1e-2)
+
+
+def test_multi_split_runs_spec4(oracle_impl):
+    """The speculative-decoding workload (64 sequences, 4 drafted tokens) on the split runs at the
+    device's wave count and at 256 waves (units of up to 16 partials)."""
+    w = make_multi_config("multi_spec4")
+    for gw in (0, 256):
+        _check(w, oracle_impl, f"spec4/w{gw}", grid_waves=gw)
+
+
+def test_multi_split_runs_bad_entry():
+    """A table entry outside the pool among a sequence's blocks gives NaN for every row of that
+    sequence (all of its units read the block); the other sequences keep their results."""
+    w = make_multi([300, 900, 450], [4, 4, 4], 8, 2, 128, 16, torch.bfloat16, seed=17)
+    _, _, good = run_multi(w)
+    assert torch.isfinite(good).all()
+    for gw in (0, 8):
+        for blk in (0, 900 // 16 - 2):
+            bt = w.block_tables.copy()
+            bt[1, blk] = w.num_blocks + 3
+            _, _, out = run_multi(w, tables=bt, grid_waves=gw)
+            say(f"[gpu] multi split bad entry: waves={gw} block={blk}")
+            assert torch.isnan(out[4:8]).all(), (gw, blk)
+            assert torch.isfinite(out[:4]).all() and torch.isfinite(out[8:]).all(), (gw, blk)
+            assert torch.allclose(out[:4], good[:4], atol=2e-3, rtol=1e-2)
+            assert torch.allclose(out[8:], good[8:], atol=2e-3, rtol=1e-2)
