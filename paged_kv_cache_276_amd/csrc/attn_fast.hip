@@ -989,7 +989,10 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
 // and block of 16 * MW query rows, chunk c of the sequence's tiles) has MW
 // waves of 16 rows and the tile pipeline of decode_prefix_kernel: each
 // 16-token tile of the chunk is read once into LDS, by all of the workgroup's
-// threads, for all of its rows.  MW is 1 when a sequence's rows fit one wave
+// threads, for all of its rows.  Tiles are computed in pairs, so that P.V
+// runs on the 32-deep matrix instruction (v_mfma_f32_16x16x32_bf16: twice the
+// work of the 16-deep one in the same cycles); an odd last tile is paired with
+// a masked one.  MW is 1 when a sequence's rows fit one wave
 // (speculative decoding: no wave only loads, and the small workgroups all fit
 // on the chip at once), else 4 or 16 (up to 256 rows per tile read).  Row r of
 // a block is new token r / G (position ctx - q_len + r / G) and head r % G; a
@@ -999,8 +1002,9 @@ template <int BS, int G, int MW>
 __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
     constexpr int T = 64 * MW;        // threads: MW waves of 16 rows each
     constexpr int TPI = 1024 / T;     // tokens of one dword column each thread moves per tile
-    constexpr int kAhead = MW == 1 ? 2 : 4;  // tiles in flight (32 / 8 / 2 load registers per tile)
+    constexpr int kAhead = MW == 1 ? 2 : 4;  // tiles in flight, whole pairs (32 / 8 / 2 load registers per tile)
     static_assert(MW == 1 || MW == 4 || MW == 16, "waves per workgroup");
+    static_assert(kAhead % 2 == 0, "tiles are loaded and computed in pairs");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -1028,17 +1032,20 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     if (ntile <= 0) return;
     const bool computes = row0 + 16 * wv < rows;
 
+    // Tile j of the chunk sits in LDS buffer j % 4: two pairs, the one being
+    // computed and the one being stored.
     __shared__ uint2 toff_lds[kPrefixChunkTilesMax];
     __shared__ int tbad_lds[kPrefixChunkTilesMax];
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
-    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][kHd * kVtRow];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[4][kTok * kKRow];
+    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[4][kHd * kVtRow];
 
     const int32_t* __restrict__ bt = a.block_tables;
     if (tid < ntile) {
         const int tok0 = (t0 + tid) * kTok;
         const int phys = bt[(int64_t)i * maxB + tok0 / BS];
         const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
-        const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * kHd;
+        // dword offset of the tile's 16 rows in the pools (two bf16 per dword)
+        const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * (kHd / 2);
         toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
         tbad_lds[tid] = badp;
     }
@@ -1049,6 +1056,7 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     const bool real = row < rows;
     const int jq = real ? row / G : 0;
     const int pos = ctx - ql + jq;  // last token this row sees
+    const int pos_lim = real ? pos : -1;  // a padding row sees nothing
     uint4 qc[4];
     {
         const uint16_t* qrow =
@@ -1070,27 +1078,33 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     struct TileKV {
         uint32_t k[TPI], v[TPI];
     };
+    // The tile's base is wave-uniform (scalar registers); lanes add 32-bit offsets.
+    const uint32_t lane_off = (uint32_t)(TPI * tg) * (kHd / 2) + (uint32_t)vj;
     auto load_tile = [&](int j, TileKV& t) {
         const uint2 o = toff_lds[j];
-        const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)(TPI * tg) * (kHd / 2) + vj;
+        const uint64_t tile = ((uint64_t)__builtin_amdgcn_readfirstlane(o.y) << 32) | __builtin_amdgcn_readfirstlane(o.x);
+        const uint32_t* kt = k32 + tile;
+        const uint32_t* vt = v32 + tile;
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) t.k[k] = k32[off + k * (kHd / 2)];
+        for (int k = 0; k < TPI; ++k) t.k[k] = kt[lane_off + k * (kHd / 2)];
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) t.v[k] = v32[off + k * (kHd / 2)];
+        for (int k = 0; k < TPI; ++k) t.v[k] = vt[lane_off + k * (kHd / 2)];
     };
     // K rows go to LDS as stored (padded rows); V goes transposed (one row
     // per dim, 16 tokens).  Value rows past the end of the context (the tail
-    // of the last tile) are stored as zeros: their weights are zero, and
-    // 0 * (whatever the slot holds, NaN included) must not reach the sums.
-    // Key rows there only give scores that the mask replaces.
+    // of the last tile), and all of a tile past the chunk's end (the masked
+    // partner of an odd last tile), are stored as zeros: their weights are
+    // zero, and 0 * (whatever the slot holds, NaN included) must not reach
+    // the sums.  Key rows there only give scores that the mask replaces.
     auto store_tile = [&](int buf, const TileKV& t, int j) {
         unsigned char* kb = &k_lds[buf][(TPI * tg) * kKRow + 4 * vj];
 #pragma unroll
         for (int k = 0; k < TPI; ++k) *reinterpret_cast<uint32_t*>(kb + k * kKRow) = t.k[k];
         const int tokb = (t0 + j) * kTok + TPI * tg;
+        const int vend = j < ntile ? ctx : 0;
         uint32_t v[TPI];
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) v[k] = tokb + k < ctx ? t.v[k] : 0u;
+        for (int k = 0; k < TPI; ++k) v[k] = tokb + k < vend ? t.v[k] : 0u;
         unsigned char* vb = &vt_lds[buf][0];
         if constexpr (TPI == 1) {  // token tg: chunk tg / 4, position tg % 4
             *reinterpret_cast<uint16_t*>(vb + vt_off(2 * vj, tg >> 2) + 2 * (tg & 3)) = (uint16_t)(v[0] & 0xffffu);
@@ -1114,27 +1128,37 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     float l = 0.f;
     bool bad = false;
 
-    auto step = [&](int buf, int j) {
-        bad = bad || tbad_lds[j] != 0;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // Tiles j (even) and j + 1: S^T of each by four 16x16x32 MFMAs, the
+    // online softmax over the lane's eight scores, then P.V as one 32-deep
+    // product per 16 dims.  In that product the lane's eight k values are
+    // tokens 4 grp .. 4 grp + 3 of tile j, then the same tokens of tile j + 1
+    // -- in P (its scores) and in V (chunk grp of both transposed tiles) alike.
+    auto step = [&](int j) {
+        const int ba = j & 3, bb = (j + 1) & 3;
+        const bool has_b = j + 1 < ntile;  // uniform
+        bad |= (tbad_lds[j] | (has_b ? tbad_lds[j + 1] : 0)) != 0;
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
-            const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qc[kq]), sc, 0, 0, 0);
+            const uint4 ka = *reinterpret_cast<const uint4*>(&k_lds[ba][r16 * kKRow + kq * 64 + grp * 16]);
+            const uint4 kb = *reinterpret_cast<const uint4*>(&k_lds[bb][r16 * kKRow + kq * 64 + grp * 16]);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qc[kq]), sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(qc[kq]), sb, 0, 0, 0);
         }
-        const int tok = (t0 + j) * kTok + 4 * grp;
-        float s[4];
-        bool vis[4];
-        bool need = false;
+        // Token r of tile j (of tile j + 1) is visible when r <= lim_a (lim_b):
+        // the causal limit, with padding rows and a missing second tile seeing
+        // nothing.
+        const int lim_a = pos_lim - ((t0 + j) * kTok + 4 * grp);
+        const int lim_b = has_b ? lim_a - kTok : -1;
+        float s[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            vis[r] = real && tok + r <= pos;
-            s[r] = vis[r] ? sc[r] * qscale : -INFINITY;
-            need = need || (vis[r] && s[r] > m + kLazyRescale);
+            s[r] = r <= lim_a ? sa[r] * qscale : -INFINITY;
+            s[4 + r] = r <= lim_b ? sb[r] * qscale : -INFINITY;
         }
-        if (__any(need)) {
-            float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-            tm = max_xor32(max_xor16(tm));
+        const float smax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+        if (__any(smax > m + kLazyRescale)) {
+            const float tm = max_xor32(max_xor16(smax));
             const float mn = tm > m + kLazyRescale ? tm : m;
             const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
             m = mn;
@@ -1146,49 +1170,63 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
                 for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
             }
         }
-        s16x4 phi, plo;
+        // m stays -inf only while the row has seen no token: then every score
+        // is -inf and every weight 0.
+        const float mref = m == -INFINITY ? 0.f : m;
+        // p = hi + lo, both bf16: each product with V is exact, the sums fp32.
+        uint32_t hi[8], lo[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float pr = vis[r] ? fast_exp2(s[r] - m) : 0.f;
+        for (int r = 0; r < 8; ++r) {
+            const float pr = fast_exp2(s[r] - mref);
             l += pr;
             const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
-            phi[r] = (short)(hb >> 16);
-            plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
+            hi[r] = hb >> 16;
+            lo[r] = __float_as_uint(pr - __uint_as_float(hb)) >> 16;
         }
+        const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+        const uint4 plo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
 #pragma unroll
         for (int jb = 0; jb < kHd / 16; ++jb) {
-            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
-            const s16x4 vv = __builtin_bit_cast(s16x4, vb);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
+            const uint2 va = *reinterpret_cast<const uint2*>(&vt_lds[ba][vt_off(16 * jb + r16, grp)]);
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[bb][vt_off(16 * jb + r16, grp)]);
+            const bf16x8 vv = as_bf16x8(make_uint4(va.x, va.y, vb.x, vb.y));
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi), vv, acc[jb], 0, 0, 0);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo), vv, acc[jb], 0, 0, 0);
         }
     };
 
-    // kAhead tiles in flight: every step issues one tile's loads (clamped to
-    // the last tile, so every path issues the same loads and each wait counts
-    // exactly the loads it needs), the loop runs in whole groups of kAhead and
-    // a tail finishes the last kAhead - 1 tiles.
+    // kAhead tiles in flight, loaded and computed in pairs: every pair step
+    // stores its two tiles, issues the loads of the pair kAhead tiles ahead
+    // (clamped to the last tile, so every path issues the same loads and each
+    // wait counts exactly the loads it needs), then computes.  A pair's
+    // buffers are rewritten two pair steps later, after the barrier that
+    // every wave passes only once its step on them is done.  The loop runs in
+    // whole groups of kAhead tiles; a tail finishes the remaining pairs.
+    const int ntile2 = ntile + (ntile & 1);  // tiles rounded up to whole pairs
     TileKV R[kAhead];
 #pragma unroll
     for (int q = 0; q < kAhead; ++q) load_tile(min(q, ntile - 1), R[q]);
     int j0 = 0;
-    for (; j0 + kAhead <= ntile; j0 += kAhead) {
+    for (; j0 + kAhead <= ntile2; j0 += kAhead) {
 #pragma unroll
-        for (int q = 0; q < kAhead; ++q) {
+        for (int q = 0; q < kAhead; q += 2) {
             const int j = j0 + q;
-            store_tile(j & 1, R[q], j);
+            store_tile(j & 3, R[q], j);
+            store_tile((j + 1) & 3, R[q + 1], j + 1);
             load_tile(min(j + kAhead, ntile - 1), R[q]);
+            load_tile(min(j + 1 + kAhead, ntile - 1), R[q + 1]);
             __syncthreads();
-            if (computes) step(j & 1, j);
+            if (computes) step(j);
         }
     }
 #pragma unroll
-    for (int q = 0; q < kAhead - 1; ++q) {
+    for (int q = 0; q + 2 < kAhead; q += 2) {
         const int j = j0 + q;
-        if (j < ntile) {  // uniform
-            store_tile(j & 1, R[q], j);
+        if (j < ntile2) {  // uniform
+            store_tile(j & 3, R[q], j);
+            store_tile((j + 1) & 3, R[q + 1], j + 1);
             __syncthreads();
-            if (computes) step(j & 1, j);
+            if (computes) step(j);
         }
     }
 
