@@ -386,10 +386,10 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (total_q < 0 || max_q_len < 1) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / cache->num_kv_heads;
-    // Waves per workgroup (16 query rows each): one when a sequence's rows fit
-    // a wave (speculative decoding: every wave then loads its own tiles and
-    // all workgroups fit on the chip at once), 4, or 16 so that up to 256 rows
-    // share each tile read.
+    // Groups of 16 query rows per workgroup: one when a sequence's rows fit a
+    // group (speculative decoding: every wave then loads its own tiles and
+    // all workgroups fit on the chip at once), 4 (one wave each), or 16 (two
+    // per wave, 8 waves) so that up to 256 rows share each tile read.
     const int64_t rows_max = (int64_t)max_q_len * group;
     const int32_t waves = rows_max <= 16 ? 1 : rows_max <= 64 ? 4 : 16;
     const int64_t rb = (rows_max + 16 * waves - 1) / (16 * waves);
@@ -436,7 +436,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     mp->base.partition_tokens = (int32_t)ct * 16;
     mp->base.max_partitions = mp->max_chunks;
     mp->base.grid_blocks = (int64_t)num_seqs * cache->num_kv_heads * rb * mc;
-    mp->base.threads_per_block = 64 * waves;
+    mp->base.threads_per_block = 64 * (waves == 16 ? 8 : waves);
     mp->base.workspace_bytes = mp->total;
     return PKV_OK;
 }

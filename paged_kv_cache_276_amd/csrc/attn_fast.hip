@@ -986,24 +986,34 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
 }
 
 // Several new tokens per sequence, causal.  Workgroup (sequence i, KV head g
-// and block of 16 * MW query rows, chunk c of the sequence's tiles) has MW
-// waves of 16 rows and the tile pipeline of decode_prefix_kernel: each
-// 16-token tile of the chunk is read once into LDS, by all of the workgroup's
-// threads, for all of its rows.  Tiles are computed in pairs, so that P.V
-// runs on the 32-deep matrix instruction (v_mfma_f32_16x16x32_bf16: twice the
-// work of the 16-deep one in the same cycles); an odd last tile is paired with
-// a masked one.  MW is 1 when a sequence's rows fit one wave
-// (speculative decoding: no wave only loads, and the small workgroups all fit
-// on the chip at once), else 4 or 16 (up to 256 rows per tile read).  Row r of
-// a block is new token r / G (position ctx - q_len + r / G) and head r % G; a
+// and block of 16 * NRG query rows, chunk c of the sequence's tiles) has the
+// tile pipeline of decode_prefix_kernel: each 16-token tile of the chunk is
+// read once into LDS, by all of the workgroup's threads, for all of its rows.
+// The rows are dealt in groups of 16: one group per wave when NRG is 1 or 4,
+// two per wave when NRG is 16 (8 waves), so that each K and V fragment read
+// from LDS feeds two matrix products.  NRG is 1 when a sequence's rows fit one
+// group (speculative decoding: no wave only loads, and the small workgroups
+// all fit on the chip at once), else 4 or 16 (up to 256 rows per tile read).
+// Tiles are computed in pairs, so that P.V runs on the 32-deep matrix
+// instruction (v_mfma_f32_16x16x32_bf16: twice the work of the 16-deep one in
+// the same cycles); an odd last tile is paired with a masked one.  Row r of a
+// block is new token r / G (position ctx - q_len + r / G) and head r % G; a
 // row sees the tokens up to its own position (the others are masked in the
 // scores).  Each row leaves the chunk's (m, l, acc) for multi_merge_kernel.
-template <int BS, int G, int MW>
-__global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
-    constexpr int T = 64 * MW;        // threads: MW waves of 16 rows each
+template <int NRG>
+struct MultiShape {
+    static constexpr int RG = NRG == 16 ? 2 : 1;  // row groups per wave
+    static constexpr int MW = NRG / RG;           // waves per workgroup
+};
+
+template <int BS, int G, int NRG>
+__global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
+    constexpr int RG = MultiShape<NRG>::RG;
+    constexpr int MW = MultiShape<NRG>::MW;
+    constexpr int T = 64 * MW;        // threads
     constexpr int TPI = 1024 / T;     // tokens of one dword column each thread moves per tile
-    constexpr int kAhead = MW == 1 ? 2 : 4;  // tiles in flight, whole pairs (32 / 8 / 2 load registers per tile)
-    static_assert(MW == 1 || MW == 4 || MW == 16, "waves per workgroup");
+    constexpr int kAhead = MW == 1 ? 2 : 4;  // tiles in flight, whole pairs (32 / 8 / 4 load registers per tile)
+    static_assert(NRG == 1 || NRG == 4 || NRG == 16, "row groups per workgroup");
     static_assert(kAhead % 2 == 0, "tiles are loaded and computed in pairs");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1023,14 +1033,15 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     // Sequences the merge reports as NaN, and blocks with no rows or tiles (uniform).
     if (q0 < 0 || q1 > a.total_q || ql < 1 || ql > a.max_q_len || ctx < ql || ctx > table_tokens) return;
     const int rows = ql * G;
-    const int row0 = 16 * MW * rb;  // first row of this workgroup
+    const int row0 = 16 * NRG * rb;  // first row of this workgroup
     if (row0 >= rows) return;
     const int nt_total = (ctx + kTok - 1) / kTok;
     const int t0 = c * CT;
     const int t1 = min(t0 + CT, nt_total);
     const int ntile = t1 - t0;
     if (ntile <= 0) return;
-    const bool computes = row0 + 16 * wv < rows;
+    const int wrow0 = row0 + 16 * RG * wv;  // first row of this wave
+    const bool computes = wrow0 < rows;
 
     // Tile j of the chunk sits in LDS buffer j % 4: two pairs, the one being
     // computed and the one being stored.
@@ -1049,22 +1060,24 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
         toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
         tbad_lds[tid] = badp;
     }
-    // This lane's row (for the scores and the softmax state): new token jq, head hq.
+    // This lane's row in each of the wave's groups (for the scores and the
+    // softmax state): new token jq, head row % G.
     const int r16 = lane & 15;
     const int grp = lane >> 4;
-    const int row = row0 + 16 * wv + r16;
-    const bool real = row < rows;
-    const int jq = real ? row / G : 0;
-    const int pos = ctx - ql + jq;  // last token this row sees
-    const int pos_lim = real ? pos : -1;  // a padding row sees nothing
-    uint4 qc[4];
-    {
+    int pos_lim[RG];  // last token the row sees; -1 for a padding row
+    uint4 qc[RG][4];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        const int row = wrow0 + 16 * rg + r16;
+        const bool real = row < rows;
+        const int jq = real ? row / G : 0;
+        pos_lim[rg] = real ? ctx - ql + jq : -1;
         const uint16_t* qrow =
             static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? row % G : 0)) * kHd;
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
             const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
-            qc[kq] = real ? v : make_uint4(0, 0, 0, 0);
+            qc[rg][kq] = real ? v : make_uint4(0, 0, 0, 0);
         }
     }
     __syncthreads();
@@ -1109,6 +1122,11 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
         if constexpr (TPI == 1) {  // token tg: chunk tg / 4, position tg % 4
             *reinterpret_cast<uint16_t*>(vb + vt_off(2 * vj, tg >> 2) + 2 * (tg & 3)) = (uint16_t)(v[0] & 0xffffu);
             *reinterpret_cast<uint16_t*>(vb + vt_off(2 * vj + 1, tg >> 2) + 2 * (tg & 3)) = (uint16_t)(v[0] >> 16);
+        } else if constexpr (TPI == 2) {  // tokens 2 tg, 2 tg + 1: chunk tg / 2, positions 2 (tg % 2) ..
+            const uint32_t even = (v[0] & 0xffffu) | (v[1] << 16);
+            const uint32_t odd = (v[0] >> 16) | (v[1] & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(vb + vt_off(2 * vj, tg >> 1) + 4 * (tg & 1)) = even;
+            *reinterpret_cast<uint32_t*>(vb + vt_off(2 * vj + 1, tg >> 1) + 4 * (tg & 1)) = odd;
         } else {
 #pragma unroll
             for (int k = 0; k < TPI; k += 4) {
@@ -1121,77 +1139,95 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
         }
     };
 
-    f32x4 acc[kHd / 16];
+    f32x4 acc[RG][kHd / 16];
+    float m[RG], l[RG];
 #pragma unroll
-    for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    float l = 0.f;
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+        for (int jb = 0; jb < kHd / 16; ++jb) acc[rg][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[rg] = -INFINITY;
+        l[rg] = 0.f;
+    }
     bool bad = false;
 
-    // Tiles j (even) and j + 1: S^T of each by four 16x16x32 MFMAs, the
-    // online softmax over the lane's eight scores, then P.V as one 32-deep
-    // product per 16 dims.  In that product the lane's eight k values are
-    // tokens 4 grp .. 4 grp + 3 of tile j, then the same tokens of tile j + 1
-    // -- in P (its scores) and in V (chunk grp of both transposed tiles) alike.
+    // Tiles j (even) and j + 1: S^T of each by four 16x16x32 MFMAs per row
+    // group, the online softmax over the lane's eight scores, then P.V as one
+    // 32-deep product per 16 dims.  In that product the lane's eight k values
+    // are tokens 4 grp .. 4 grp + 3 of tile j, then the same tokens of tile
+    // j + 1 -- in P (its scores) and in V (chunk grp of both transposed tiles)
+    // alike.
     auto step = [&](int j) {
         const int ba = j & 3, bb = (j + 1) & 3;
         const bool has_b = j + 1 < ntile;  // uniform
         bad |= (tbad_lds[j] | (has_b ? tbad_lds[j + 1] : 0)) != 0;
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sa[RG], sb[RG];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) sa[rg] = sb[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
             const uint4 ka = *reinterpret_cast<const uint4*>(&k_lds[ba][r16 * kKRow + kq * 64 + grp * 16]);
             const uint4 kb = *reinterpret_cast<const uint4*>(&k_lds[bb][r16 * kKRow + kq * 64 + grp * 16]);
-            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qc[kq]), sa, 0, 0, 0);
-            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(qc[kq]), sb, 0, 0, 0);
-        }
-        // Token r of tile j (of tile j + 1) is visible when r <= lim_a (lim_b):
-        // the causal limit, with padding rows and a missing second tile seeing
-        // nothing.
-        const int lim_a = pos_lim - ((t0 + j) * kTok + 4 * grp);
-        const int lim_b = has_b ? lim_a - kTok : -1;
-        float s[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[r] = r <= lim_a ? sa[r] * qscale : -INFINITY;
-            s[4 + r] = r <= lim_b ? sb[r] * qscale : -INFINITY;
-        }
-        const float smax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-        if (__any(smax > m + kLazyRescale)) {
-            const float tm = max_xor32(max_xor16(smax));
-            const float mn = tm > m + kLazyRescale ? tm : m;
-            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m - mn);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * grp + r, kWave);
-#pragma unroll
-                for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
+            for (int rg = 0; rg < RG; ++rg) {
+                sa[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qc[rg][kq]), sa[rg], 0, 0, 0);
+                sb[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), as_bf16x8(qc[rg][kq]), sb[rg], 0, 0, 0);
             }
         }
-        // m stays -inf only while the row has seen no token: then every score
-        // is -inf and every weight 0.
-        const float mref = m == -INFINITY ? 0.f : m;
-        // p = hi + lo, both bf16: each product with V is exact, the sums fp32.
-        uint32_t hi[8], lo[8];
+        uint4 phi[RG], plo[RG];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float pr = fast_exp2(s[r] - mref);
-            l += pr;
-            const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
-            hi[r] = hb >> 16;
-            lo[r] = __float_as_uint(pr - __uint_as_float(hb)) >> 16;
+        for (int rg = 0; rg < RG; ++rg) {
+            // Token r of tile j (of tile j + 1) is visible when r <= lim_a
+            // (lim_b): the causal limit, with padding rows and a missing
+            // second tile seeing nothing.
+            const int lim_a = pos_lim[rg] - ((t0 + j) * kTok + 4 * grp);
+            const int lim_b = has_b ? lim_a - kTok : -1;
+            float s[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[r] = r <= lim_a ? sa[rg][r] * qscale : -INFINITY;
+                s[4 + r] = r <= lim_b ? sb[rg][r] * qscale : -INFINITY;
+            }
+            const float smax =
+                fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+            if (__any(smax > m[rg] + kLazyRescale)) {
+                const float tm = max_xor32(max_xor16(smax));
+                const float mn = tm > m[rg] + kLazyRescale ? tm : m[rg];
+                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rg] - mn);
+                m[rg] = mn;
+                l[rg] *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) acc[rg][jb][r] *= ar;
+                }
+            }
+            // m stays -inf only while the row has seen no token: then every
+            // score is -inf and every weight 0.
+            const float mref = m[rg] == -INFINITY ? 0.f : m[rg];
+            // p = hi + lo, both bf16: each product with V is exact, the sums fp32.
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float pr = fast_exp2(s[r] - mref);
+                l[rg] += pr;
+                const uint32_t hb = __float_as_uint(pr) & 0xffff0000u;
+                hi[r] = hb >> 16;
+                lo[r] = __float_as_uint(pr - __uint_as_float(hb)) >> 16;
+            }
+            phi[rg] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+            plo[rg] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
         }
-        const uint4 phi = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
-        const uint4 plo = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
 #pragma unroll
         for (int jb = 0; jb < kHd / 16; ++jb) {
             const uint2 va = *reinterpret_cast<const uint2*>(&vt_lds[ba][vt_off(16 * jb + r16, grp)]);
             const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[bb][vt_off(16 * jb + r16, grp)]);
             const bf16x8 vv = as_bf16x8(make_uint4(va.x, va.y, vb.x, vb.y));
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi), vv, acc[jb], 0, 0, 0);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo), vv, acc[jb], 0, 0, 0);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                acc[rg][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[rg]), vv, acc[rg][jb], 0, 0, 0);
+                acc[rg][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[rg]), vv, acc[rg][jb], 0, 0, 0);
+            }
         }
     };
 
@@ -1231,20 +1267,24 @@ __global__ __launch_bounds__(64 * MW) void multi_query_kernel(const DecodeArgs a
     }
 
     if (!computes) return;
-    const float lt = sum_xor32(sum_xor16(l));
     const int MC = a.prefix_max_chunks;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int r = row0 + 16 * wv + 4 * grp + rr;
-        if (r < rows) {
-            const int64_t pr = ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + c;
+    for (int rg = 0; rg < RG; ++rg) {
+        const float lt = sum_xor32(sum_xor16(l[rg]));
 #pragma unroll
-            for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[jb][rr];
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = wrow0 + 16 * rg + 4 * grp + rr;
+            if (r < rows) {
+                const int64_t pr = ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + c;
+#pragma unroll
+                for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[rg][jb][rr];
+            }
         }
-    }
-    if (lane < 16 && real) {
-        const int64_t pr = ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + row % G) * MC + c;
-        a.ws_pml[pr] = make_float2(m, bad ? NAN : lt);
+        const int row = wrow0 + 16 * rg + lane;
+        if (lane < 16 && row < rows) {
+            const int64_t pr = ((int64_t)(q0 + row / G) * Hq + (int64_t)g * G + row % G) * MC + c;
+            a.ws_pml[pr] = make_float2(m[rg], bad ? NAN : lt);
+        }
     }
 }
 
@@ -1740,7 +1780,7 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     switch (a.multi_waves) {
         case 1: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1>), grid, dim3(64), 0, stream, a, a.scale * kLog2e); break;
         case 4: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4>), grid, dim3(256), 0, stream, a, a.scale * kLog2e); break;
-        case 16: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16>), grid, dim3(1024), 0, stream, a, a.scale * kLog2e); break;
+        case 16: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, a.scale * kLog2e); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();

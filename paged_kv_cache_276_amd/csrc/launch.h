@@ -46,7 +46,7 @@ struct DecodeArgs {
     int32_t total_q;
     int32_t max_q_len;
     int32_t multi_row_blocks;    // row blocks (16 * multi_waves rows each) per KV head
-    int32_t multi_waves;         // waves per workgroup of the multi-query kernel: 1, 4 or 16
+    int32_t multi_waves;         // 16-row groups per workgroup of the multi-query kernel: 1, 4 or 16 (1, 4, 8 waves)
     int32_t multi_split_runs;    // 1: equal runs of tiles over the resident waves (multi_waves 1),
                                  // partials in ws_rec / ws_ml / ws_acc with 16 rows per slot
 };
