@@ -258,10 +258,11 @@ pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const vo
  * longest table, grid_blocks = workgroups of the chunk kernel,
  * workspace_bytes.  Shapes as PKV_KERNEL_FAST with block_size 16, 32 or 64
  * (PKV_ERR_UNSUPPORTED otherwise).  The rows of a KV head, max_q_len *
- * (num_q_heads / num_kv_heads), go to workgroups of 1, 4 or 16 waves of 16
- * rows (the fewest that hold them, at most 16), in row blocks; at most 65535
+ * (num_q_heads / num_kv_heads), go to workgroups of 1, 4 or 16 groups of 16
+ * rows (the fewest that hold them, at most 16; 16 groups are 8 waves of two
+ * groups each, so grid threads = 64, 256 or 512), in row blocks; at most 65535
  * row blocks in all.  opts->partition_tokens, if nonzero, sets the chunk (a
- * multiple of 16, at most 1024).
+ * multiple of 16, at most 2048).
  * With one wave per row block (max_q_len * G <= 16) and no chunk asked for,
  * the 16-token tiles of all (sequence, KV head) pairs are instead split in
  * equal runs over opts->grid_waves waves (0: the waves the device keeps

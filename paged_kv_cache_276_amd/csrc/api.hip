@@ -247,6 +247,11 @@ struct PrefixPlan {
 
 constexpr int32_t kPrefixChunkTilesMax = 64;
 constexpr int64_t kPrefixTargetWorkgroups = 512;  // about two per CU of the largest parts
+constexpr int32_t kMultiChunkTilesMax = 128;
+// Multi-query workgroups of 16 row groups (8 waves of 254 registers) fit one
+// per CU: aim for one round of them on the largest parts, so that fewer
+// chunks leave fewer partials to write and merge.
+constexpr int64_t kMultiWideTargetWorkgroups = 256;
 
 pkv_status make_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                             int32_t num_groups, int32_t max_prefix_tokens, const pkv_cache_desc* cache,
@@ -419,11 +424,12 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     const int64_t tiles = ((int64_t)max_blocks_per_seq * cache->block_size + 15) / 16;
     int64_t ct;
     if (chunk_tokens) {
-        if (chunk_tokens < 0 || chunk_tokens % 16 != 0 || chunk_tokens / 16 > kPrefixChunkTilesMax) return PKV_ERR_SHAPE;
+        if (chunk_tokens < 0 || chunk_tokens % 16 != 0 || chunk_tokens / 16 > kMultiChunkTilesMax) return PKV_ERR_SHAPE;
         ct = chunk_tokens / 16;
     } else {
-        ct = (tiles * num_seqs * cache->num_kv_heads * rb + kPrefixTargetWorkgroups - 1) / kPrefixTargetWorkgroups;
-        ct = ct < 8 ? 8 : (ct > kPrefixChunkTilesMax ? kPrefixChunkTilesMax : ct);
+        const int64_t target = waves == 16 ? kMultiWideTargetWorkgroups : kPrefixTargetWorkgroups;
+        ct = (tiles * num_seqs * cache->num_kv_heads * rb + target - 1) / target;
+        ct = ct < 8 ? 8 : (ct > kMultiChunkTilesMax ? kMultiChunkTilesMax : ct);
     }
     const int64_t mc = (tiles + ct - 1) / ct;
     if (mc > 65535) return PKV_ERR_SHAPE;

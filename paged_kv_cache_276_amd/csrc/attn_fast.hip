@@ -763,6 +763,7 @@ constexpr int kPrefixWaves = 4;
 constexpr int kPrefixThreads = kPrefixWaves * 64;
 constexpr int kPrefixAhead = 4;           // tiles in flight per workgroup
 constexpr int kPrefixChunkTilesMax = 64;  // LDS table size
+constexpr int kMultiChunkTilesMax = 128;  // LDS table size of the multi-query chunk kernel
 constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes): conflict-free fragment reads
 // LDS row of the transposed V tile: one dim, 16 tokens (32 bytes), padded to
 // 40 bytes.  Rows 10 banks apart put the 16 rows that one P.V operand read
@@ -1045,20 +1046,20 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
 
     // Tile j of the chunk sits in LDS buffer j % 4: two pairs, the one being
     // computed and the one being stored.
-    __shared__ uint2 toff_lds[kPrefixChunkTilesMax];
-    __shared__ int tbad_lds[kPrefixChunkTilesMax];
+    __shared__ uint2 toff_lds[kMultiChunkTilesMax];
+    __shared__ int tbad_lds[kMultiChunkTilesMax];
     __shared__ __attribute__((aligned(16))) unsigned char k_lds[4][kTok * kKRow];
     __shared__ __attribute__((aligned(16))) unsigned char vt_lds[4][kHd * kVtRow];
 
     const int32_t* __restrict__ bt = a.block_tables;
-    if (tid < ntile) {
-        const int tok0 = (t0 + tid) * kTok;
+    for (int t = tid; t < ntile; t += T) {  // ntile <= kMultiChunkTilesMax (the plan's chunk limit)
+        const int tok0 = (t0 + t) * kTok;
         const int phys = bt[(int64_t)i * maxB + tok0 / BS];
         const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
         // dword offset of the tile's 16 rows in the pools (two bf16 per dword)
         const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * (kHd / 2);
-        toff_lds[tid] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
-        tbad_lds[tid] = badp;
+        toff_lds[t] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
+        tbad_lds[t] = badp;
     }
     // This lane's row in each of the wave's groups (for the scores and the
     // softmax state): new token jq, head row % G.

@@ -147,6 +147,9 @@ def test_multi_plan_split_runs(L):
         assert plan.workspace_bytes >= units * 8 + slots * 16 * (128 * 4 + 8)
     st, plan = mplan(4, chunk=256)
     assert st == 0 and plan.partition_tokens == 256 and plan.threads_per_block == 64
+    assert mplan(4, chunk=2048)[0] == 0 and mplan(4, chunk=2064)[0] == 2 and mplan(4, chunk=40)[0] == 2
+    st, plan = mplan(64)  # 256 rows: 16 groups of 16 rows as 8 waves of two groups
+    assert st == 0 and plan.threads_per_block == 512
     st, plan = mplan(5)  # 20 rows: four waves per workgroup, chunks
     assert st == 0 and plan.threads_per_block == 256 and plan.partition_tokens != 16
     assert mplan(4, waves=8193)[0] == 2

@@ -71,7 +71,9 @@ CASES = [
 def test_multi_cases(case, oracle_impl):
     lengths, qls, hq, hkv, B = CASES[case]
     w = make_multi(lengths, qls, hq, hkv, 128, B, torch.bfloat16, seed=200 + case, pool_fill=0.7)
-    for ct in (0, 16, 64):
+    # 1040 and 2048 tokens: chunks of 65 and 128 tiles (an odd last pair; more tiles than a
+    # one-wave workgroup has threads for its table)
+    for ct in (0, 16, 64, 1040, 2048):
         _check(w, oracle_impl, f"case{case}/ct{ct}", chunk_tokens=ct)
 
 
