@@ -235,6 +235,74 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int r16 = lane & 15;  // MFMA column (token) / V column group
     const int grp = lane >> 4;  // MFMA k-group / V token phase
 
+    // Issue the K and V loads of a tile from its record (element offset of
+    // its 16 K/V rows in the pools, flags, second block of a split tile).
+    // The tile's base address is wave-uniform: it goes to scalar registers,
+    // the loads take 32-bit lane offsets.
+    auto issue_rec = [&](const uint4 rv, TileLoad& T) {
+        const uint32_t tlo = __builtin_amdgcn_readfirstlane(rv.x);
+        const uint32_t thi = __builtin_amdgcn_readfirstlane(rv.y);
+        T.flags = __builtin_amdgcn_readfirstlane(rv.z);
+        const int64_t tile_s = (int64_t)(((uint64_t)thi << 32) | tlo);
+        const int valid = (int)(T.flags & 0xffu);
+        const uint16_t* kt = kbase + tile_s;
+        const uint16_t* vt = vbase + tile_s;
+        const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
+        if constexpr (kSplit) {
+            // Rows BS.. of the tile live in the second block: they take
+            // `diff` more elements than rows of the first block would.
+            const int64_t tile2 = (int64_t)__builtin_amdgcn_readfirstlane(rv.w) * (BS * kHd);
+            const int64_t diff = tile2 - (tile_s + (int64_t)BS * kHd);
+            const int64_t kx = r16 >= BS ? diff : 0;
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32 + kx);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int vr = min(4 * ii + grp, valid - 1);
+                const int64_t voff = (int64_t)vr * kHd + r16 * 8 + (vr >= BS ? diff : 0);
+                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+            }
+        } else {
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
+                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+            }
+        }
+    };
+
+    // Each segment's first tile is issued before the segment's set-up (walk,
+    // table entries, q rows), so that its latency overlaps the set-up; its
+    // record is built from the cursor, exactly as the set-up builds it.  Every
+    // segment enters the tile loop the same way, with that tile's loads
+    // issued before the set-up's own loads, which keeps the loop's load waits
+    // exact.
+    auto issue_first = [&](const Cursor& C, TileLoad& T) {
+        const int tok0 = C.start + C.b * kTok;
+        const int64_t row = (int64_t)C.i * maxB + tok0 / BS;
+        const int phys = bt[row];
+        bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
+        const int ph = badp ? 0 : phys;
+        uint32_t second = 0u;
+        if constexpr (kSplit) {
+            int ph2 = ph;
+            if (tok0 + BS < C.ctx) {
+                const int phys2 = bt[row + 1];
+                const bool bad2 = (unsigned)phys2 >= (unsigned)a.num_blocks;
+                badp = badp || bad2;
+                ph2 = bad2 ? 0 : phys2;
+            }
+            second = (uint32_t)((int64_t)ph2 * Hkv + C.g);
+        }
+        const int64_t off = (((int64_t)ph * Hkv + C.g) * BS + (tok0 % BS)) * kHd;
+        const uint32_t flags = (uint32_t)min(kTok, C.ctx - tok0) | (C.b == 0 ? kFirst : 0u) |
+                               (C.b == C.n - 1 ? kLast : 0u) | (badp ? kBad : 0u);
+        issue_rec(make_uint4((uint32_t)off, (uint32_t)((uint64_t)off >> 32), flags, second), T);
+    };
+    TileLoad X0, X1;
+
     // Per-segment tables in LDS (one wave per workgroup):
     //   rec[k]   tile k: element offset of its 16 K/V rows in the pools (x, y),
     //            valid rows | run << 8 | flags (z)
@@ -347,6 +415,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     };
 
     for (int64_t seg0 = c0; seg0 < c1;) {
+        issue_first(P, X0);  // the cursor is at the segment's first tile
+        __builtin_amdgcn_sched_barrier(0);
         // ---- segment set-up: walk up to kSegRuns runs (pieces of units) and
         // kSegTiles tiles, then request every block-table entry and q row of
         // the segment at once and park them in LDS.
@@ -448,6 +518,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             if (r < nruns)
 #pragma unroll
                 for (int v = 0; v < kQv; ++v) q_lds[r][v * kWave + lane] = qv[r][v];
+        // Every load of the set-up (and the first tile's, issued before it)
+        // is complete here, on every path into the tile loop, so the loop's
+        // waits count only its own tiles.
+        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -456,40 +530,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // Issue the K and V loads of segment tile kk.  The tile's base address
         // is wave-uniform: it goes to scalar registers, the loads take 32-bit
         // lane offsets.
-        auto issue = [&](int kk, TileLoad& T) {
-            const uint4 rv = rec_lds[kk];
-            const uint32_t tlo = __builtin_amdgcn_readfirstlane(rv.x);
-            const uint32_t thi = __builtin_amdgcn_readfirstlane(rv.y);
-            T.flags = __builtin_amdgcn_readfirstlane(rv.z);
-            const int64_t tile_s = (int64_t)(((uint64_t)thi << 32) | tlo);
-            const int valid = (int)(T.flags & 0xffu);
-            const uint16_t* kt = kbase + tile_s;
-            const uint16_t* vt = vbase + tile_s;
-            const uint32_t koff = (uint32_t)(r16 * kHd + grp * 8);
-            if constexpr (kSplit) {
-                // Rows BS.. of the tile live in the second block: they take
-                // `diff` more elements than rows of the first block would.
-                const int64_t tile2 = (int64_t)__builtin_amdgcn_readfirstlane(rv.w) * (BS * kHd);
-                const int64_t diff = tile2 - (tile_s + (int64_t)BS * kHd);
-                const int64_t kx = r16 >= BS ? diff : 0;
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32 + kx);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int vr = min(4 * ii + grp, valid - 1);
-                    const int64_t voff = (int64_t)vr * kHd + r16 * 8 + (vr >= BS ? diff : 0);
-                    T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
-                }
-            } else {
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
-                    T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
-                }
-            }
-        };
+        auto issue = [&](int kk, TileLoad& T) { issue_rec(rec_lds[kk], T); };
 
         // Entering a tile: at a unit's first tile (or the chunk's first) take
         // the unit's q from LDS and reset the running state.
@@ -619,9 +660,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             __builtin_amdgcn_sched_barrier(0);
             if (kk < seg_len) step(seg0 + kk, cur);
         };
-        TileLoad X0, X1;
-        issue(0, X0);
-        __builtin_amdgcn_sched_barrier(0);
         for (int kk = 0; kk < seg_len; kk += 2) {
             phase(kk, X0, X1);
             phase(kk + 1, X1, X0);
