@@ -153,6 +153,16 @@ def test_multi_split_runs_spec4(oracle_impl):
         _check(w, oracle_impl, f"spec4/w{gw}", grid_waves=gw)
 
 
+def test_multi_split_runs_many_sequences(oracle_impl):
+    """150 sequences: the split-run kernel reads the lengths in chunks of 64 sequences."""
+    rng = np.random.Generator(np.random.PCG64(83))
+    qls = rng.integers(1, 4, size=150, endpoint=True)
+    lengths = [int(q) + int(rng.integers(0, 300)) for q in qls]
+    w = make_multi(lengths, qls.tolist(), 8, 2, 128, 16, torch.bfloat16, seed=83, pool_fill=0.8)
+    for gw in (0, 40):
+        _check(w, oracle_impl, f"many/w{gw}", grid_waves=gw)
+
+
 def test_multi_split_runs_bad_entry():
     """A table entry outside the pool among a sequence's blocks gives NaN for every row of that
     sequence (all of its units read the block); the other sequences keep their results."""

@@ -118,6 +118,19 @@ def test_partition_sweep(T, oracle_impl):
         _check_step(w, oracle_impl, f"sweep/k{k}/T{T}", partition_tokens=T, kernel=k)
 
 
+def test_large_batch(oracle_impl):
+    """More than 512 sequences: the fast kernel's lengths pass, search and unit walk then read the
+    lengths from global memory in chunks of 512 instead of keeping them in LDS.  Short and empty
+    sequences mixed, several wave counts (one not a multiple of 8)."""
+    rng = np.random.Generator(np.random.PCG64(81))
+    lengths = rng.integers(0, 100, size=1100, endpoint=True).tolist()
+    w = make_custom(lengths, 8, 2, 128, 16, torch.bfloat16, seed=81, pool_fill=0.8)
+    assert w.num_seqs > 2 * 512
+    for waves in (0, 7, 64, 2048):
+        _check_step(w, oracle_impl, f"large/waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
+    _check_step(w, oracle_impl, "large/generic", kernel=pkv.PKV_KERNEL_GENERIC)
+
+
 def test_needles(oracle_impl):
     """One dominant key at block and partition edges: dropping or misplacing any block fails."""
     B, T, n = 16, 256, 3001

@@ -89,6 +89,18 @@ def test_prefix_cases(case, oracle_impl):
             _check(w, oracle_impl, f"case{case}/ct{ct}/w{waves}", chunk_tokens=ct, grid_waves=waves)
 
 
+def test_prefix_large_batch(oracle_impl):
+    """600 sequences in 75 groups of 8 sharing a two-block prefix: the suffix pass reads the
+    lengths and the prefix starts from global memory (more than 512 sequences)."""
+    rng = np.random.Generator(np.random.PCG64(82))
+    P, B = 64, 32
+    lens = (P + rng.integers(1, 40, size=600, endpoint=True)).tolist()
+    groups = [(P, list(range(8 * k, 8 * k + 8))) for k in range(75)]
+    w = make_custom(lens, 8, 2, 128, B, torch.bfloat16, seed=82, prefix_groups=groups, pool_fill=0.8)
+    for waves in (0, 24):
+        _check(w, oracle_impl, f"large/w{waves}", grid_waves=waves)
+
+
 def test_groups_split_in_eights(oracle_impl):
     """A prompt with 20 samples is described as groups of 8, 8 and 4."""
     w = make_custom([530 + 7 * i for i in range(20)], 8, 2, 128, 16, torch.bfloat16, seed=9,
