@@ -92,7 +92,9 @@ typedef struct pkv_decode_opts {
                                  0 = library choice */
     int32_t kernel;           /* a PKV_KERNEL_* value */
     int32_t grid_waves;       /* fast kernel: number of waves that share the work, 1 ..
-                                 PKV_MAX_GRID_WAVES; 0 = as many as the device keeps resident */
+                                 PKV_MAX_GRID_WAVES; 0 = library choice: as many as the device
+                                 keeps resident, or half of them when num_seqs * num_kv_heads
+                                 is at most a quarter of that (fewer, longer units) */
     int32_t xcd_balance;      /* fast kernel: work share of each wave on an odd-numbered XCD, in
                                  64ths of an equal share (waves on even XCDs get 128 minus it),
                                  1 .. 127; 64 = equal shares; 0 = library choice
@@ -117,7 +119,7 @@ typedef struct pkv_decode_plan {
                                  fast: most partial results one (sequence, KV head) can leave */
     int32_t threads_per_block;
     int64_t grid_blocks;      /* generic: workgroups of the partition kernel; fast: the requested
-                                 wave count, or 0 when the device decides (resident waves) */
+                                 wave count, or 0 for the library's choice (see grid_waves) */
     uint64_t workspace_bytes; /* required workspace (0 when nothing needs merging) */
 } pkv_decode_plan;
 

@@ -4,7 +4,8 @@
 // Work decomposition.  The unit of work is a tile: 16 consecutive logical
 // tokens of one (sequence, KV head).  All tiles are laid end to end in the
 // order (sequence, KV head, tile) and the grid's W waves each take one
-// contiguous run of them (W = the waves the device keeps resident), so the
+// contiguous run of them (W = the waves the device keeps resident, or half of
+// them for few long units: see launch_t), so the
 // load is balanced whatever the length mix: a long sequence spreads over many
 // waves, many short ones share a wave.  The runs are equal, or weighted by the
 // wave's XCD (odd XCDs read more slowly; Split in tile_math.h).  Each wave
@@ -1846,13 +1847,22 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G, PREFIX>);
-    int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+    int waves = a.grid_waves;
+    if (waves <= 0) {
+        // The resident waves (two per SIMD), or one per SIMD when there are at most a
+        // quarter as many (sequence, KV head) units: long units then span half as many
+        // waves and leave half as many partials.  Measured on one box: 8 x 32k 194.5 ->
+        // 190.2 us and 64 sequences of U[128, 4096] 103.2 -> 101.3 us with one per SIMD;
+        // 256 sequences (2,048 units) 294.9 against 295.6 us with two.
+        waves = resident_waves(k);
+        if (waves >= 16 && units * 4 <= waves) waves = waves / 2 / 8 * 8;
+    }
     if (waves <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX>), dim3(waves), dim3(kWave), 0, stream, a,
                        a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     hipLaunchKernelGGL((merge_fast_kernel<G, PREFIX>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
                        a.max_blocks_per_seq * BS);
     return hipGetLastError();
