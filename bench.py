@@ -517,7 +517,7 @@ def main(argv=None) -> int:
             "kernel": plan["kernel"],
             "partition_tokens": plan["partition_tokens"],
             "grid_waves": plan["grid_blocks"],
-            "xcd_balance": args.xcd_balance or pkv.XCD_BALANCE_DEFAULT,
+            "xcd_balance": args.xcd_balance or "library choice",
         },
         "roofline": {
             "kernel": ("paged_attn_decode_prefix (prefix, suffix and merge kernels, one call; unique bytes)"

@@ -98,9 +98,10 @@ typedef struct pkv_decode_opts {
     int32_t xcd_balance;      /* fast kernel: work share of each wave on an odd-numbered XCD, in
                                  64ths of an equal share (waves on even XCDs get 128 minus it),
                                  1 .. 127; 64 = equal shares; 0 = library choice
-                                 (PKV_XCD_BALANCE_DEFAULT).  Applies when the wave count is a
-                                 multiple of 8 and there are at least as many tiles as waves;
-                                 results do not depend on it. */
+                                 (PKV_XCD_BALANCE_DEFAULT with two waves per SIMD, equal shares
+                                 when the library launches one per SIMD).  Applies when the
+                                 wave count is a multiple of 8 and there are at least as many
+                                 tiles as waves; results do not depend on it. */
 } pkv_decode_opts;
 
 /* On the MI355X boxes measured, waves on odd-numbered XCDs drained the same reads 4-9% more

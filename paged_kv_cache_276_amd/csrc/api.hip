@@ -219,7 +219,7 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
     a.part_tokens = plan.partition_tokens;
     a.max_parts = plan.max_partitions;
     a.grid_waves = opts ? opts->grid_waves : 0;
-    a.xcd_balance = opts && opts->xcd_balance ? opts->xcd_balance : PKV_XCD_BALANCE_DEFAULT;
+    a.xcd_balance = opts ? opts->xcd_balance : 0;  // 0: the launch decides
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -350,7 +350,7 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
     a.part_tokens = 16;
     a.max_parts = pkv::kMaxGridWaves;
     a.grid_waves = opts ? opts->grid_waves : 0;
-    a.xcd_balance = opts && opts->xcd_balance ? opts->xcd_balance : PKV_XCD_BALANCE_DEFAULT;
+    a.xcd_balance = opts ? opts->xcd_balance : 0;  // 0: the launch decides
     a.seq_start = seq_prefix_tokens;
     a.groups = groups;
     a.num_groups = num_groups;

@@ -50,6 +50,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "pagedkv.h"
 #include "tile_math.h"
 
 namespace pkv {
@@ -1849,6 +1850,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G, PREFIX>);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
     int waves = a.grid_waves;
+    bool one_per_simd = false;
     if (waves <= 0) {
         // The resident waves (two per SIMD), or one per SIMD when there are at most a
         // quarter as many (sequence, KV head) units: long units then span half as many
@@ -1856,11 +1858,19 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
         // 190.2 us and 64 sequences of U[128, 4096] 103.2 -> 101.3 us with one per SIMD;
         // 256 sequences (2,048 units) 294.9 against 295.6 us with two.
         waves = resident_waves(k);
-        if (waves >= 16 && units * 4 <= waves) waves = waves / 2 / 8 * 8;
+        if (waves >= 16 && units * 4 <= waves) {
+            waves = waves / 2 / 8 * 8;
+            one_per_simd = true;
+        }
     }
     if (waves <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX>), dim3(waves), dim3(kWave), 0, stream, a,
-                       a.scale * kLog2e);
+    // The library's XCD shares: with two waves per SIMD, odd XCDs drain more slowly
+    // (PKV_XCD_BALANCE_DEFAULT); with one per SIMD, equal shares measured best (8 x 32k:
+    // 187.5 us against 188.7 at 60/64 and 189.0 at 62/64; 64 sequences: a tie).
+    DecodeArgs b = a;
+    if (b.xcd_balance == 0) b.xcd_balance = one_per_simd ? 64 : PKV_XCD_BALANCE_DEFAULT;
+    hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX>), dim3(waves), dim3(kWave), 0, stream, b,
+                       b.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((merge_fast_kernel<G, PREFIX>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,

@@ -31,7 +31,7 @@ struct DecodeArgs {
     int32_t part_tokens;
     int32_t max_parts;
     int32_t grid_waves;  // fast kernel: requested waves (0 = resident capacity)
-    int32_t xcd_balance; // fast kernel: share of a wave on an odd XCD, in 64ths (64 = equal)
+    int32_t xcd_balance; // fast kernel: share of a wave on an odd XCD, in 64ths (64 = equal); 0 = library choice
     // Shared-prefix path (paged_attn_decode_prefix); zero/null otherwise.
     const int32_t* seq_start;    // [S] tokens of each sequence covered by its group's shared prefix
     const int32_t* groups;       // [num_groups][2] first sequence, member count
