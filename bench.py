@@ -473,6 +473,7 @@ def main(argv=None) -> int:
     K = args.steps
     tm = timed_steps(write, decode, K)
     print(f"[bench] timed {K} steps", file=sys.stderr, flush=True)
+    launched = pkv.last_launch_info()  # the grid and XCD shares the library chose
     ms_per_step = tm["ms_per_step"]
     dec_avg = tm["decode_ms"]
     nbytes = algorithmic_bytes(w)
@@ -516,8 +517,8 @@ def main(argv=None) -> int:
             "table_entries": int(((w.context_lens.astype(np.int64) + w.block_size - 1) // w.block_size).sum()),
             "kernel": plan["kernel"],
             "partition_tokens": plan["partition_tokens"],
-            "grid_waves": plan["grid_blocks"],
-            "xcd_balance": args.xcd_balance or "library choice",
+            "grid_waves": launched["grid"] if launched["kernel"] == "fast" else plan["grid_blocks"],
+            "xcd_balance": launched["xcd_balance"] if launched["kernel"] == "fast" else None,
         },
         "roofline": {
             "kernel": ("paged_attn_decode_prefix (prefix, suffix and merge kernels, one call; unique bytes)"

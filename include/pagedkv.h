@@ -315,6 +315,26 @@ pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const voi
                                    float *out, void *workspace, uint64_t workspace_bytes,
                                    const pkv_cache_desc *cache, const pkv_decode_opts *opts, void *stream);
 
+/*
+ * What the calling thread's last successful paged_attn_decode or
+ * paged_attn_decode_prefix call launched (host struct), so that a caller can
+ * see which kernel ran and the launch choices the library made:
+ *   kernel            PKV_KERNEL_FAST or PKV_KERNEL_GENERIC (0 before any call)
+ *   grid              fast: waves sharing the tiles; generic: workgroups of the
+ *                     partition kernel
+ *   xcd_balance       fast: the odd-XCD share used, in 64ths (64 = equal); 0 generic
+ *   partition_tokens  fast: 16 (tokens per tile); generic: tokens per partition
+ * Per thread and per process; NULL info gives PKV_ERR_NULL.  For callers that
+ * check or report the path taken (for example a benchmark).
+ */
+typedef struct pkv_launch_info {
+    int32_t kernel;
+    int32_t grid;
+    int32_t xcd_balance;
+    int32_t partition_tokens;
+} pkv_launch_info;
+pkv_status pkv_last_launch_info(pkv_launch_info *info);
+
 /* Human-readable name of a status code (static string). */
 const char *pkv_status_string(pkv_status status);
 

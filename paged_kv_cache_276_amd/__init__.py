@@ -53,6 +53,7 @@ __all__ = [
     "paged_attn_plan",
     "paged_attn_workspace_bytes",
     "cache_desc",
+    "last_launch_info",
     "version",
     "PkvError",
 ]
@@ -62,6 +63,16 @@ _DTYPES = {torch.float32: _lib.PKV_F32, torch.bfloat16: _lib.PKV_BF16}
 
 def version() -> str:
     return _lib.lib().pkv_version().decode()
+
+
+def last_launch_info() -> Dict[str, object]:
+    """What this thread's last paged_attn_decode / paged_attn_decode_prefix call launched: kernel
+    family, grid (fast: waves; generic: partition workgroups), the odd-XCD share used and the
+    tokens per tile or partition."""
+    info = _lib.LaunchInfo()
+    _lib.check(_lib.lib().pkv_last_launch_info(ctypes.byref(info)), "pkv_last_launch_info")
+    return {"kernel": _lib.KERNEL_NAMES.get(info.kernel, "none"), "grid": info.grid,
+            "xcd_balance": info.xcd_balance, "partition_tokens": info.partition_tokens}
 
 
 def cache_desc(k_cache: torch.Tensor) -> CacheDesc:

@@ -32,6 +32,7 @@ EXPORTS = (
     "paged_block_copy",
     "pkv_status_string",
     "pkv_version",
+    "pkv_last_launch_info",
     "pkv_bm_create",
     "pkv_bm_destroy",
     "pkv_bm_num_free",
@@ -70,6 +71,11 @@ class DecodePlan(ctypes.Structure):
         ("grid_blocks", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
     ]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("grid", ctypes.c_int32), ("xcd_balance", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32)]
 
 
 class PkvError(RuntimeError):
@@ -140,6 +146,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_status_string.argtypes = [ctypes.c_int]
     L.pkv_version.restype = ctypes.c_char_p
     L.pkv_version.argtypes = []
+    L.pkv_last_launch_info.restype = ctypes.c_int
+    L.pkv_last_launch_info.argtypes = [P(LaunchInfo)]
     _lib = L
     return L
 

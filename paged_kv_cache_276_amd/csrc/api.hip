@@ -228,8 +228,28 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
     } else {
         e = pkv::launch_decode_generic(a, s);
         if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
+        if (e == hipSuccess)
+            pkv::last_launch() = pkv::LaunchInfo{PKV_KERNEL_GENERIC, (int32_t)plan.grid_blocks, 0,
+                                                 plan.partition_tokens};
     }
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+namespace pkv {
+LaunchInfo& last_launch() {
+    thread_local LaunchInfo info{0, 0, 0, 0};
+    return info;
+}
+}  // namespace pkv
+
+PKV_API pkv_status pkv_last_launch_info(pkv_launch_info* info) {
+    if (!info) return PKV_ERR_NULL;
+    const pkv::LaunchInfo& l = pkv::last_launch();
+    info->kernel = l.kernel;
+    info->grid = l.grid;
+    info->xcd_balance = l.xcd_balance;
+    info->partition_tokens = l.partition_tokens;
+    return PKV_OK;
 }
 
 namespace {

@@ -62,6 +62,13 @@ hipError_t launch_block_copy(void* k_cache, void* v_cache, const int32_t* pairs,
                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
 // Returns hipErrorInvalidValue when no instantiation matches the shape.
+// The calling thread's last decode launch (kernel family, grid, XCD share,
+// partition tokens), set by the launchers and read by pkv_last_launch_info.
+struct LaunchInfo {
+    int32_t kernel, grid, xcd_balance, partition_tokens;
+};
+LaunchInfo& last_launch();
+
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream);
 // Shared-prefix decode: prefix kernel, suffix tiles (fast kernel), merge.

@@ -131,6 +131,28 @@ def test_large_batch(oracle_impl):
     _check_step(w, oracle_impl, "large/generic", kernel=pkv.PKV_KERNEL_GENERIC)
 
 
+def test_launch_info_reports_the_library_choices():
+    """Few (sequence, KV head) units launch one wave per SIMD with equal XCD shares, many units two
+    per SIMD with the default share; an explicit request is launched as asked, and the generic
+    kernel reports its partition grid."""
+    few = make_custom([300] * 4, 8, 2, 128, 16, torch.bfloat16, seed=95)       # 8 units
+    many = make_custom([40] * 1100, 8, 2, 128, 16, torch.bfloat16, seed=96)    # 2,200 units
+    run_step(few, kernel=pkv.PKV_KERNEL_FAST)
+    a = pkv.last_launch_info()
+    run_step(many, kernel=pkv.PKV_KERNEL_FAST)
+    b = pkv.last_launch_info()
+    say(f"[gpu] launch info: few units {a}, many units {b}")
+    assert a["kernel"] == b["kernel"] == "fast" and a["partition_tokens"] == 16
+    assert a["grid"] % 8 == 0 and b["grid"] == 2 * a["grid"]
+    assert a["xcd_balance"] == 64 and b["xcd_balance"] == pkv.XCD_BALANCE_DEFAULT
+    run_step(few, kernel=pkv.PKV_KERNEL_FAST, grid_waves=40, xcd_balance=30)
+    c = pkv.last_launch_info()
+    assert c["grid"] == 40 and c["xcd_balance"] == 30
+    run_step(few, kernel=pkv.PKV_KERNEL_GENERIC, partition_tokens=64)
+    d = pkv.last_launch_info()
+    assert d["kernel"] == "generic" and d["partition_tokens"] == 64 and d["grid"] > 0
+
+
 def test_needles(oracle_impl):
     """One dominant key at block and partition edges: dropping or misplacing any block fails."""
     B, T, n = 16, 256, 3001
