@@ -57,8 +57,3 @@ def kv_bytes_per_request(bytes_per_token: int, active_tokens: int) -> int:
 
 def cache_limited_concurrency(available_bytes: int, bytes_per_request: int) -> int:
     return available_bytes // bytes_per_request
-
-
-def slot_to_block_offset(slot: int, block_size: int):
-    """Reading of the slot encoding: slot = physical_block * block_size + offset."""
-    return slot // block_size, slot % block_size

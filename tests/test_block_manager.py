@@ -10,6 +10,16 @@
   write into a shared, partly filled block moves the writer to a fresh copy
   (page "praveentn.live/architecture/quiz/pagedattention-kv-cache-constraint",
   section "What the change bought").
+* Freeing worked by hand: a finished request's blocks return to the pool and
+  the next request takes them, lowest id first; a block that another table
+  still names stays held until its last holder is freed (page
+  "x321.org/?p=939", section "PagedAttention borrows an operating-system
+  trick"; page "praveentn.live/...", section "What the change bought").
+* The block copy worked by hand: the destination becomes a bit copy of the
+  source in K and V, every other block keeps its bits, and pairs run in the
+  order given, so a chain of copies carries the first source's bits along
+  (same section of the praveentn.live page: a shared block is copied before
+  it is written).
 * The library equals the reference on seeded random operation sequences
   (tables, lengths, slots, copies, reference counts, failures), and keeps the
   bookkeeping invariants.
@@ -17,13 +27,14 @@
 
 import os
 import re
+import sys
 
 import numpy as np
 import pytest
 
 import oracle
 from oracle.arith import blocks_needed
-from oracle.blocks import NoBlocks, RefBlockManager
+from oracle.blocks import NoBlocks, RefBlockManager, copy_blocks
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -59,6 +70,14 @@ def _append(m, kind, sids):
         return m.append(sids)
     s, c = m.append(sids)
     return list(map(int, s)), [tuple(map(int, p)) for p in c]
+
+
+def _num_free(m, kind):
+    return len(m.free_ids()) if kind == "ref" else m.num_free
+
+
+def _refcount(m, kind, b):
+    return m.ref[b] if kind == "ref" else m.refcount(b)
 
 
 KINDS = ["ref", "lib"]
@@ -110,6 +129,53 @@ def test_copy_on_write_by_hand(kind, lib_built):
     assert copies == [(1, 3), (1, 4)] and slots == [3 * B + 3, 4 * B + 3, 1 * B + 3]
     slots, copies = _append(m, kind, [1, 3, 4])  # all last blocks full: each takes a new block, no copies
     assert copies == [] and slots == [5 * B, 6 * B, 7 * B]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_free_returns_blocks_for_reuse(kind, lib_built):
+    B = 4
+    m = _mgr(kind, 8, B)
+    m.add(1, 10)                     # blocks 0, 1, 2
+    m.add(2, 5)                      # blocks 3, 4
+    assert _num_free(m, kind) == 3
+    m.free(1)                        # the request ends: its three blocks are free again
+    assert _num_free(m, kind) == 6 and [_refcount(m, kind, b) for b in range(3)] == [0, 0, 0]
+    m.add(3, 6)                      # the next request reuses them, lowest first
+    assert _table(m, kind, 3, 4)[0] == [0, 1, -1, -1]
+    m.fork(2, 4)                     # blocks 3 and 4 named by two tables
+    assert _refcount(m, kind, 3) == _refcount(m, kind, 4) == 2
+    m.free(2)                        # one holder left: the blocks stay taken
+    assert _refcount(m, kind, 3) == _refcount(m, kind, 4) == 1 and _num_free(m, kind) == 4
+    m.add(5, 8)                      # two blocks, neither of the held ones
+    assert _table(m, kind, 5, 4)[0] == [2, 5, -1, -1]
+    m.free(4)                        # the last holder: now 3 and 4 return to the pool
+    assert _refcount(m, kind, 3) == _refcount(m, kind, 4) == 0 and _num_free(m, kind) == 4
+    m.add(6, 7)
+    assert _table(m, kind, 6, 4)[0] == [3, 4, -1, -1]
+    slots, copies = _append(m, kind, [6])  # sole holder of a partly filled block: written in place
+    assert copies == [] and slots == [4 * B + 3]
+
+
+def test_copy_blocks_by_hand():
+    nb, hkv, B, d = 6, 2, 4, 8
+    k = np.arange(nb * hkv * B * d, dtype=np.uint16).reshape(nb, hkv, B, d)
+    v = (k.astype(np.uint32) + 40000).astype(np.uint16)
+    # bit patterns that a float copy could alter: bf16 NaN with payload, -0.0, a subnormal
+    k[1, 0, 0, :3] = [0x7FC1, 0x8000, 0x0001]
+    v[1, 1, 3, :3] = [0xFFA5, 0x8000, 0x0003]
+    k0, v0 = k.copy(), v.copy()
+    copy_blocks(k, v, [(1, 3)])
+    assert np.array_equal(k[3], k0[1]) and np.array_equal(v[3], v0[1])
+    for b in (0, 1, 2, 4, 5):        # the source and every other block are untouched
+        assert np.array_equal(k[b], k0[b]) and np.array_equal(v[b], v0[b])
+    k1, v1 = k.copy(), v.copy()
+    copy_blocks(k, v, [(0, 2), (2, 5)])  # in order: 5 receives what 2 holds after the first copy
+    assert np.array_equal(k[2], k1[0]) and np.array_equal(v[2], v1[0])
+    assert np.array_equal(k[5], k1[0]) and np.array_equal(v[5], v1[0])
+    for b in (0, 1, 3, 4):
+        assert np.array_equal(k[b], k1[b]) and np.array_equal(v[b], v1[b])
+    copy_blocks(k, v, [])
+    assert np.array_equal(k[5], k1[0])
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -225,6 +291,14 @@ MUTANTS = {
     "fork_not_counted": ("            self.ref[b] += 1\n", "            pass\n"),
     "highest_free_first": ("self.ref[free[0]] = 1\n        return free[0]", "self.ref[free[-1]] = 1\n        return free[-1]"),
     "add_floor_blocks": ("need = -(-n // self.B)", "need = n // self.B"),
+    "free_not_counted": ("for b in self.tables.pop(sid):\n            self.ref[b] -= 1",
+                         "for b in self.tables.pop(sid):\n            pass"),
+    "free_releases_shared": ("for b in self.tables.pop(sid):\n            self.ref[b] -= 1",
+                             "for b in self.tables.pop(sid):\n            self.ref[b] = 0"),
+    "copy_src_dst_swapped": ("k_cache[dst] = k_cache[src]\n        v_cache[dst] = v_cache[src]",
+                             "k_cache[src] = k_cache[dst]\n        v_cache[src] = v_cache[dst]"),
+    "copy_v_not_copied": ("        v_cache[dst] = v_cache[src]", "        pass"),
+    "copy_pairs_reversed": ("for src, dst in pairs:", "for src, dst in reversed(list(pairs)):"),
 }
 
 
@@ -236,13 +310,18 @@ def test_reference_pins_catch_mutants(name, monkeypatch, lib_built):
     assert old in src
     ns = {}
     exec(compile(src.replace(old, new), "mutant_blocks.py", "exec"), ns)
-    monkeypatch.setattr(__import__(__name__), "RefBlockManager", ns["RefBlockManager"])
-    monkeypatch.setattr(__import__(__name__), "NoBlocks", ns["NoBlocks"])
+    mod = sys.modules[__name__]
+    monkeypatch.setattr(mod, "RefBlockManager", ns["RefBlockManager"])
+    monkeypatch.setattr(mod, "NoBlocks", ns["NoBlocks"])
+    monkeypatch.setattr(mod, "copy_blocks", ns["copy_blocks"])
     failed = False
-    for t in (test_pages_block_counts, test_growth_keeps_ceil_blocks, test_copy_on_write_by_hand,
-              test_exhaustion_is_all_or_nothing):
+    pins = [(t, ("ref", True)) for t in (test_pages_block_counts, test_growth_keeps_ceil_blocks,
+                                          test_copy_on_write_by_hand, test_free_returns_blocks_for_reuse,
+                                          test_exhaustion_is_all_or_nothing)]
+    pins.append((test_copy_blocks_by_hand, ()))
+    for t, args in pins:
         try:
-            t("ref", True)
+            t(*args)
         except (Exception, pytest.fail.Exception):
             failed = True
     assert failed, f"mutant {name} passed every pin"
