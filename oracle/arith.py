@@ -57,3 +57,11 @@ def kv_bytes_per_request(bytes_per_token: int, active_tokens: int) -> int:
 
 def cache_limited_concurrency(available_bytes: int, bytes_per_request: int) -> int:
     return available_bytes // bytes_per_request
+
+
+def slot_to_block_offset(slot: int, block_size: int):
+    """Slot encoding read as slot = physical_block * block_size + offset (the pages give the
+    block table, not a slot number): physical block and offset of a slot."""
+    if slot < 0 or block_size <= 0:
+        raise ValueError("slot >= 0 and block_size > 0 required")
+    return slot // block_size, slot % block_size

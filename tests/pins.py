@@ -158,6 +158,23 @@ def pin_block_map(o) -> None:
         np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
 
 
+def pin_slot_encoding(arith) -> None:
+    """The seven-slot example with slots numbered physical block * B + offset: logical token j
+    of request A is in pool block table[j // B] at offset j % B, so A2 (pool block 5) holds
+    token 2B + 3 in slot 5B + 3, which decodes to (5, 3).  Every token of A decodes to the
+    block the diagram names for it, never to a decoy (B1, C2, free), at its own offset."""
+    g = _golden("block_map.json")
+    table = g["block_table"]
+    for b in (4, 16):
+        assert arith.slot_to_block_offset(5 * b + 3, b) == (5, 3)
+        seen = set()
+        for j in range(4 * b):
+            blk, off = arith.slot_to_block_offset(table[j // b] * b + j % b, b)
+            assert g["pool_slots"][blk] == g["logical_blocks"][j // b] and off == j % b
+            seen.add((blk, off))
+        assert len(seen) == 4 * b
+
+
 def pin_brute_force(o) -> None:
     """Oracle on scattered blocks == SDPA on the contiguous data, many shapes."""
     rng = np.random.default_rng(11)
@@ -462,4 +479,4 @@ ORACLE_PINS = [
     pin_multi_one_token_is_decode, pin_multi_sdpa_causal, pin_multi_rows_are_truncated_decodes,
     pin_multi_errors,
 ]
-ARITH_PINS = [pin_block_arithmetic, pin_kv_bytes]
+ARITH_PINS = [pin_block_arithmetic, pin_kv_bytes, pin_slot_encoding]

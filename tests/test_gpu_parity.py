@@ -110,6 +110,23 @@ def test_shapes(case, oracle_impl):
             _check_step(w, oracle_impl, f"shape{case}/k{k}/T{T}", partition_tokens=T, kernel=k)
 
 
+G2_CASES = [(4, 2, 16), (8, 4, 32), (8, 4, 8), (4, 2, 64)]  # (Hq, Hkv, B): two query heads per KV head
+
+
+@pytest.mark.parametrize("hq,hkv,B", G2_CASES)
+def test_fast_group_size_2(hq, hkv, B, oracle_impl):
+    """bf16, head_dim 128, two query heads per KV head: the library picks the fast kernel's G = 2
+    instantiation (its own stage depth, q-row mask and flush layout) and its merge; lengths at
+    tile and block edges and past 4k, at the library's wave count and at 1, 3, 8 and 64 waves."""
+    lengths = [1, 2, 15, 16, 17, 31, 32, 33, 64, 255, 257, 1000, 2047, 2048, 4099, 5000]
+    w = make_custom(lengths, hq, hkv, 128, B, torch.bfloat16, seed=200 + B + hq, pool_fill=0.7)
+    for waves in (0, 1, 3, 8, 64):
+        _check_step(w, oracle_impl, f"g2/Hq{hq}/Hkv{hkv}/B{B}/waves{waves}", grid_waves=waves)
+        info = pkv.last_launch_info()
+        assert info["kernel"] == "fast", info
+        assert waves == 0 or info["grid"] == waves, info
+
+
 @pytest.mark.parametrize("T", [64, 128, 256, 512, 1024, 4096, 8192])
 def test_partition_sweep(T, oracle_impl):
     """Split-K partition sizes agree with the oracle (and so with each other)."""
