@@ -62,6 +62,8 @@ def parse_args(argv=None):
                    help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
                         "each shared block is read once per group")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-achievable", action="store_true",
+                   help="skip the same-run streaming-read ceiling (2 GiB read by a plain HIP kernel)")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per launch measured by rocprofv3 counters (optional)")
@@ -123,8 +125,22 @@ def cpu_baseline(w) -> dict:
         "sample": f"whole batch ({w.num_seqs} seqs, write + attention), median of {len(times)} runs "
                   f"of {med:.2f} s",
         "kv_GBps": algorithmic_bytes(w)["kv"] / med / 1e9,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+        "threads_used": o.num_threads(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (the machine name where that is missing)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 DECODE_KERNELS = ("decode_prefix_kernel", "decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel")
@@ -315,6 +331,98 @@ def timed_steps(write, decode, K: int) -> dict:
     return res
 
 
+def achievable_read(dev, gib: int = 2, reps: int = 10) -> dict:
+    """Same-run ceiling: the hand-written streaming-read kernels of libpkvprobe.so over a `gib` GiB
+    buffer, three access patterns at four grid sizes; the best one's median of `reps` launches (each
+    between its own pair of HIP events)."""
+    import ctypes
+
+    from paged_kv_cache_276_amd import build as pkv_build
+
+    if not os.path.exists(pkv_build.PROBE_LIBRARY):
+        raise RuntimeError(f"{pkv_build.PROBE_LIBRARY} is not built (python -m paged_kv_cache_276_amd.build)")
+    lib = ctypes.CDLL(pkv_build.PROBE_LIBRARY)
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(cus * 16, dtype=torch.int32, device=dev)
+    he = _HipEvents()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = {0: "grid stride", 1: "contiguous per workgroup", 2: "contiguous per workgroup, non-temporal"}
+    best = None
+    tried = []
+    for variant, per_cu in [(v, p) for v in (0, 1, 2) for p in (2, 4, 8, 16)]:
+        blocks = cus * per_cu
+
+        def launch():
+            rc = lib.pkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, variant,
+                                           ctypes.c_void_p(sink.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"pkv_probe_stream_read failed ({rc})")
+
+        launch()
+        launch()
+        ev = [(he.new(), he.new()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            he.record(e0)
+            launch()
+            he.record(e1)
+        torch.cuda.synchronize()
+        ms = statistics.median(he.elapsed_ms(e0, e1) for e0, e1 in ev)
+        he.free([e for pair in ev for e in pair])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tried.append({"variant": names[variant], "workgroups": blocks, "GBps": round(gbs, 1)})
+        if best is None or gbs > best["GBps"]:
+            best = {"GBps": gbs, "bytes": nbytes, "workgroups": blocks, "us": ms * 1e3, "variant": names[variant]}
+    del buf, sink
+    best["probe"] = "stream_read_kernel (libpkvprobe.so): 16-byte loads, 8 in flight per thread, 256 threads"
+    best["tried"] = tried
+    return best
+
+
+def per_call_percentiles(fn, calls: int) -> dict:
+    """Durations of `calls` single calls, each between its own pair of HIP events (outside the timed
+    region): p10 / p50 / p90 in microseconds."""
+    he = _HipEvents()
+    ev = [(he.new(), he.new()) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        he.record(e0)
+        fn()
+        he.record(e1)
+    torch.cuda.synchronize()
+    us = sorted(he.elapsed_ms(e0, e1) * 1e3 for e0, e1 in ev)
+    he.free([e for pair in ev for e in pair])
+    return {"p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+            "p90": float(np.percentile(us, 90)), "calls": calls}
+
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def multi_roofline(flops: float, nbytes: float, seconds: float) -> dict:
+    """The roof of a call with `flops` of bf16 matrix work over `nbytes` of algorithmic bytes: HBM below
+    the ridge (8 TB/s x intensity < 2.5 PFLOP/s), the matrix cores above it; `frac` against that roof."""
+    intensity = flops / nbytes
+    if intensity * PEAK_HBM_GBS * 1e9 < PEAK_BF16_TFLOPS * 1e12:
+        achieved = nbytes / seconds / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = flops / seconds / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof.update({"kernel": "paged_attn_decode_multi (one call)", "traffic": None,
+                 "intensity_flop_per_byte": intensity,
+                 "ridge_flop_per_byte": PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)})
+    return roof
+
+
 def bench_multi(args) -> int:
     """A step with several new tokens per sequence: paged_kv_write of the new tokens, then the causal
     multi-token attention.  value = new tokens per second; the roofline prices the attention call on the
@@ -370,9 +478,7 @@ def bench_multi(args) -> int:
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_tokens": int(ctx.sum()),
                    "lengths": w.meta.get("lengths"), "chunk_tokens": plan["chunk_tokens"]},
-        "roofline": {"kernel": "paged_attn_decode_multi (chunk + merge kernels, one call)", "bound": "hbm",
-                     "achieved": (kv + qo) / att / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": (kv + qo) / att / 1e9 / PEAK_HBM_GBS, "traffic": None},
+        "roofline": multi_roofline(flops, kv + qo, att),
         "attention_us": att * 1e6,
         "mfma_TFLOPs": flops / att / 1e12,
         "mfma_frac_of_bf16_peak": flops / att / 2.5e15,
@@ -380,6 +486,7 @@ def bench_multi(args) -> int:
         "timing": {"gpu_us_per_step": tm["gpu_ms_per_step"] * 1e3, "events": tm["event_kind"],
                    "per_launch": "K launches back to back / K"},
     }
+    rec["attention_us_per_call"] = per_call_percentiles(attend, min(K, 200))
     if not args.no_parity:
         import oracle
 
@@ -542,6 +649,13 @@ def main(argv=None) -> int:
         "torch": torch.__version__,
         "hip": torch.version.hip,
     }
+
+    rec["decode_us_per_call"] = per_call_percentiles(decode, min(K, 200))
+    if not args.no_achievable:
+        ach = achievable_read(dev)
+        rec["achievable_GBps"] = ach["GBps"]
+        rec["achievable_read"] = ach
+        rec["roofline"]["pct_of_achievable"] = 100.0 * achieved / ach["GBps"]
 
     if args.cold_steps > 0:
         # The flush only reads: a written flush would leave dirty lines whose write-back

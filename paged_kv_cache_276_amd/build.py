@@ -14,6 +14,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libpagedkv.so")
+# The benchmark's streaming-read probe (achievable HBM read rate); not part of the library.
+PROBE_SOURCE = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIBRARY = os.path.join(PKG, "libpkvprobe.so")
 
 SOURCES = ["kv_write.hip", "attn_generic.hip", "attn_fast.hip", "attn_combine.hip", "api.hip", "block_manager.cpp"]
 ARCH = "gfx950"
@@ -58,7 +61,20 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIBRARY)
+    build_probe(verbose)
     return LIBRARY
+
+
+def build_probe(verbose: bool = False) -> str:
+    tmp = PROBE_LIBRARY + ".tmp"
+    cmd = [_hipcc(), *COMMON_FLAGS, "-shared", "-o", tmp, PROBE_SOURCE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SOURCE}:\n{p.stderr}")
+    os.replace(tmp, PROBE_LIBRARY)
+    return PROBE_LIBRARY
 
 
 if __name__ == "__main__":

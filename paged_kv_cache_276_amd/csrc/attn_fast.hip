@@ -1873,10 +1873,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
                        b.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, b.xcd_balance, kTok};
     hipLaunchKernelGGL((merge_fast_kernel<G, PREFIX>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
                        a.max_blocks_per_seq * BS);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, b.xcd_balance, kTok};
+    return e;
 }
 
 template <int BS, bool PREFIX>
