@@ -73,6 +73,18 @@ struct TileLoad {
     uint32_t flags;  // valid rows | run << 8 | kFirst | kLast | kBad (the tile's record)
 };
 
+// Loads marked non-temporal: K and V rows are read once per call, and
+// streaming them past the caches' replacement keeps the read rate up
+// (16-byte pieces for the decode kernel, 4-byte ones for the multi-query
+// kernels' LDS-staged tiles; the shared-prefix pass measured no gain).
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
 constexpr int kSegTiles = 128;  // tiles per segment (two per lane in the set-up)
 constexpr uint32_t kFirst = 1u << 16;  // tile 0 of its unit
 constexpr uint32_t kLast = 1u << 17;   // last tile of its unit
@@ -257,20 +269,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const int64_t diff = tile2 - (tile_s + (int64_t)BS * kHd);
             const int64_t kx = r16 >= BS ? diff : 0;
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32 + kx);
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = load_stream(kt + koff + kq * 32 + kx);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int vr = min(4 * ii + grp, valid - 1);
                 const int64_t voff = (int64_t)vr * kHd + r16 * 8 + (vr >= BS ? diff : 0);
-                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+                T.v[ii] = load_stream(vt + voff);
             }
         } else {
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) T.k[kq] = *reinterpret_cast<const uint4*>(kt + koff + kq * 32);
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = load_stream(kt + koff + kq * 32);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
-                T.v[ii] = *reinterpret_cast<const uint4*>(vt + voff);
+                T.v[ii] = load_stream(vt + voff);
             }
         }
     };
@@ -1140,9 +1152,9 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
         const uint32_t* kt = k32 + tile;
         const uint32_t* vt = v32 + tile;
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) t.k[k] = kt[lane_off + k * (kHd / 2)];
+        for (int k = 0; k < TPI; ++k) t.k[k] = load_stream(kt + lane_off + k * (kHd / 2));
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) t.v[k] = vt[lane_off + k * (kHd / 2)];
+        for (int k = 0; k < TPI; ++k) t.v[k] = load_stream(vt + lane_off + k * (kHd / 2));
     };
     // K rows go to LDS as stored (padded rows); V goes transposed (one row
     // per dim, 16 tokens).  Value rows past the end of the context (the tail
@@ -1532,9 +1544,9 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
                 const uint2 o = toff_lds[j];
                 const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) tk.k[k] = k32[off + k * (kHd / 2)];
+                for (int k = 0; k < kTok; ++k) tk.k[k] = load_stream(k32 + off + k * (kHd / 2));
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) tk.v[k] = v32[off + k * (kHd / 2)];
+                for (int k = 0; k < kTok; ++k) tk.v[k] = load_stream(v32 + off + k * (kHd / 2));
             };
             // K rows as stored (padded rows); V transposed, its rows past the
             // context stored as zeros (0 * whatever the slot holds must not

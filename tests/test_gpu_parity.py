@@ -320,20 +320,40 @@ def test_write_bit_patterns():
 
 
 def test_fast_caller_workspace_reuse(oracle_impl):
-    """A caller-owned workspace full of garbage, reused across calls with different wave counts."""
-    w = make_custom([100, 3000, 17, 640, 0], 16, 4, 128, 16, torch.bfloat16, seed=81)
-    d = to_device(w)
-    plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, d["k_cache"])
-    assert plan["kernel"] == "fast"
-    ws = torch.full(((plan["workspace_bytes"] + 15) // 16 * 16,), 0x5A, dtype=torch.uint8, device=d["q"].device)
-    pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
-    ref = oracle.decode_step(w, oracle=oracle_impl)
-    for waves in (0, 5, 64, 1, 0):
-        out = torch.full((w.num_seqs, w.num_q_heads, w.head_dim), float("nan"), device=d["q"].device)
-        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                              w.scale, out=out, workspace=ws, grid_waves=waves)
-        torch.cuda.synchronize()
-        assert_parity(out, ref.out, f"workspace reuse waves={waves}")
+    """A caller-owned workspace full of garbage, shared by a small and a larger batch, calls with
+    different wave counts and the generic kernel in between."""
+    w = make_custom([100, 3000, 17, 640, 0, 5000], 16, 4, 128, 16, torch.bfloat16, seed=81)
+    big = make_custom([300] * 200 + [2000] * 8, 16, 4, 128, 16, torch.bfloat16, seed=82)
+    ws = torch.full((64 << 20,), 0x5A, dtype=torch.uint8, device=torch.device("cuda", 0))
+    refs = {}
+    for rnd in range(2):
+        for name, ww in (("small", w), ("big", big)):
+            d = to_device(ww)
+            plan = pkv.paged_attn_plan(ww.num_seqs, ww.num_q_heads, ww.max_blocks_per_seq, d["k_cache"])
+            assert plan["kernel"] == "fast" and plan["workspace_bytes"] <= ws.numel()
+            pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
+            if name not in refs:
+                refs[name] = oracle.decode_step(ww, oracle=oracle_impl).out
+            for waves in ((0, 5, 64, 1, 3, 0) if name == "small" else (0, 333)):
+                out = torch.full((ww.num_seqs, ww.num_q_heads, ww.head_dim), float("nan"), device=d["q"].device)
+                pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                      ww.scale, out=out, workspace=ws, grid_waves=waves)
+                torch.cuda.synchronize()
+                assert_parity(out, refs[name], f"workspace reuse {name} round {rnd} waves={waves}")
+                gen = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                            d["context_lens"], ww.scale, workspace=ws,
+                                            kernel=pkv.PKV_KERNEL_GENERIC, partition_tokens=64)
+                torch.cuda.synchronize()
+                assert_parity(gen, refs[name], f"generic kernel on the shared workspace ({name}, waves={waves})")
+
+
+def test_very_large_batch(oracle_impl):
+    """8,200 sequences x 8 KV heads (65,600 units, lengths 0..40 so that units share and split waves)."""
+    rng = np.random.Generator(np.random.PCG64(83))
+    lengths = rng.integers(0, 40, size=8200, endpoint=True).tolist()
+    w = make_custom(lengths, 16, 8, 128, 16, torch.bfloat16, seed=83, pool_fill=0.9)
+    for waves in (0, 1000):
+        _check_step(w, oracle_impl, f"very large batch/waves{waves}", kernel=pkv.PKV_KERNEL_FAST, grid_waves=waves)
 
 
 def test_workspace_errors_raise():
