@@ -61,7 +61,8 @@ typedef enum pkv_status {
     PKV_ERR_HIP = 6,         /* the HIP runtime reported an error while enqueueing */
     PKV_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned */
     PKV_ERR_NO_BLOCKS = 8,   /* block manager: the pool has too few free blocks */
-    PKV_ERR_SEQ = 9          /* block manager: unknown, repeated or already existing sequence id */
+    PKV_ERR_SEQ = 9,         /* block manager: unknown, repeated or already existing sequence id */
+    PKV_ERR_TOO_LARGE = 10   /* paged_attn_decode_noalloc: the call needs more than PKV_NOALLOC_SCRATCH_BYTES */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -199,6 +200,29 @@ pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_c
                              float scale, float *out, void *workspace, uint64_t workspace_bytes,
                              const pkv_cache_desc *cache, const pkv_decode_opts *opts,
                              void *stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, with the workspace
+ * taken from a device array that the library holds on every GPU it runs on
+ * (PKV_NOALLOC_SCRATCH_BYTES, kept until the process ends).  The call
+ * allocates nothing; the first call on a device looks the array's address up
+ * (hipGetSymbolAddress) with that device current.
+ *
+ * Arguments as paged_attn_decode without workspace and workspace_bytes.  A
+ * call whose plan (paged_attn_plan) needs a workspace larger than
+ * PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_TOO_LARGE and enqueues nothing.
+ * Nothing in the array needs clearing: every byte a call reads was written
+ * earlier in that call.  All calls on one GPU share its array, so calls that
+ * may overlap on one GPU (two streams, two threads) race: serialise them.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkv_status paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     float scale, float *out, const pkv_cache_desc *cache,
+                                     const pkv_decode_opts *opts, void *stream);
 
 /*
  * paged_attn_prefix_plan -- host-only plan of paged_attn_decode_prefix: the

@@ -8,6 +8,7 @@ CPU or PyTorch fallback.
 
     paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache)
     out = paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale)
+    paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out)  # no allocation
     out = paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens,
                                    seq_prefix_tokens, groups, max_prefix_tokens, scale)
     out = paged_attn_decode_multi(q, k_cache, v_cache, block_tables, context_lens,
@@ -47,6 +48,7 @@ __all__ = [
     "paged_kv_write",
     "paged_attn_decode",
     "paged_attn_decode_multi",
+    "paged_attn_decode_noalloc",
     "paged_attn_decode_prefix",
     "paged_attn_multi_plan",
     "paged_attn_prefix_plan",
@@ -196,12 +198,8 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Optiona
     return ws
 
 
-def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                      partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
-                      grid_waves: int = 0, xcd_balance: int = 0, stream=None) -> torch.Tensor:
-    """out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i over the paged K/V of sequence i (fp32)."""
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, out):
+    """Shape, dtype and device checks shared by the decode entry points; returns (desc, S, Hq, out)."""
     dev = k_cache.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
@@ -219,6 +217,17 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         out = torch.empty((S, Hq, desc.head_dim), dtype=torch.float32, device=dev)
     _dev(out, "out", dev)
     _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, desc.head_dim), "out must be fp32 [S][Hq][D]")
+    return desc, S, Hq, out
+
+
+def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
+                      grid_waves: int = 0, xcd_balance: int = 0, stream=None) -> torch.Tensor:
+    """out[i][h] = softmax(scale * q[i][h] . K_i^T) V_i over the paged K/V of sequence i (fp32)."""
+    dev = k_cache.device
+    desc, S, Hq, out = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
     maxb = block_tables.shape[1]
     opts = _opts(partition_tokens, kernel, grid_waves, xcd_balance)
     s = _stream(dev, stream)
@@ -237,6 +246,29 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         ctypes.c_void_p(context_lens.data_ptr()), S, Hq, ctypes.c_float(scale),
         ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_bytes, ctypes.byref(desc), ctypes.byref(opts), s)
     _lib.check(st, "paged_attn_decode")
+    return out
+
+
+# Scratch bytes of the allocation-free entry point (PKV_NOALLOC_SCRATCH_BYTES in include/pagedkv.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                              out: torch.Tensor, partition_tokens: int = 0, kernel: int = PKV_KERNEL_AUTO,
+                              grid_waves: int = 0, xcd_balance: int = 0, stream=None) -> torch.Tensor:
+    """paged_attn_decode with the library's own device scratch instead of a workspace: nothing is
+    allocated, `out` included (the caller passes it).  Calls that may overlap on one GPU race."""
+    dev = k_cache.device
+    desc, S, Hq, out = _decode_args(q, k_cache, v_cache, block_tables, context_lens, out)
+    maxb = block_tables.shape[1]
+    opts = _opts(partition_tokens, kernel, grid_waves, xcd_balance)
+    st = _lib.lib().paged_attn_decode_noalloc(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()), maxb,
+        ctypes.c_void_p(context_lens.data_ptr()), S, Hq, ctypes.c_float(scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.byref(desc), ctypes.byref(opts), _stream(dev, stream))
+    _lib.check(st, "paged_attn_decode_noalloc")
     return out
 
 

@@ -25,6 +25,7 @@ EXPORTS = (
     "paged_attn_plan",
     "paged_attn_workspace_bytes",
     "paged_attn_decode",
+    "paged_attn_decode_noalloc",
     "paged_attn_prefix_plan",
     "paged_attn_decode_prefix",
     "paged_attn_multi_plan",
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode.restype = ctypes.c_int
     L.paged_attn_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, ctypes.c_float, vp, vp, u64,
                                     P(CacheDesc), P(DecodeOpts), vp]
+    L.paged_attn_decode_noalloc.restype = ctypes.c_int
+    L.paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, ctypes.c_float, vp,
+                                            P(CacheDesc), P(DecodeOpts), vp]
     L.paged_attn_prefix_plan.restype = ctypes.c_int
     L.paged_attn_prefix_plan.argtypes = [i32, i32, i32, i32, i32, P(CacheDesc), P(DecodeOpts), P(DecodePlan)]
     L.paged_attn_decode_prefix.restype = ctypes.c_int

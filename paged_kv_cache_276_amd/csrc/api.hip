@@ -3,6 +3,8 @@
 // and dispatch to the kernels.  Every check runs before anything is enqueued.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "pagedkv.h"
 #include "pagedkv_blocks.h"
@@ -173,24 +175,22 @@ PKV_API pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_he
     return PKV_OK;
 }
 
-PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                     float scale, float* out, void* workspace, uint64_t workspace_bytes,
-                                     const pkv_cache_desc* cache, const pkv_decode_opts* opts,
-                                     void* stream) {
-    pkv_decode_plan plan;
-    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, &plan);
-    if (st != PKV_OK) return st;
-    if (num_seqs == 0) return PKV_OK;
+namespace {
+
+// Checks of paged_attn_decode that come before the workspace's (same order in both entry points).
+pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, const float* out) {
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-        return PKV_ERR_ALIGN;
-    if (plan.workspace_bytes > 0) {
-        if (!workspace) return PKV_ERR_WORKSPACE;
-        if (workspace_bytes < plan.workspace_bytes) return PKV_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-    }
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_ERR_ALIGN;
+    return PKV_OK;
+}
+
+// paged_attn_decode after validation, with a workspace of at least plan.workspace_bytes.
+pkv_status decode_with_workspace(const pkv_decode_plan& plan, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 float* out, void* workspace, const pkv_cache_desc* cache,
+                                 const pkv_decode_opts* opts, void* stream) {
 
     const int32_t group = num_q_heads / cache->num_kv_heads;
     const WorkspaceLayout wl =
@@ -233,6 +233,79 @@ PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const v
                                                  plan.partition_tokens};
     }
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+PKV_API pkv_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     float scale, float* out, void* workspace, uint64_t workspace_bytes,
+                                     const pkv_cache_desc* cache, const pkv_decode_opts* opts,
+                                     void* stream) {
+    pkv_decode_plan plan;
+    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, &plan);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    st = check_decode(q, k_cache, v_cache, block_tables, context_lens, out);
+    if (st != PKV_OK) return st;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace) return PKV_ERR_WORKSPACE;
+        if (workspace_bytes < plan.workspace_bytes) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    }
+    return decode_with_workspace(plan, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, num_q_heads, scale, out, workspace, cache, opts, stream);
+}
+
+// ---- The allocation-free variant: its workspace is this file-scope device
+// array.  In host code the name `scratch` is only a stand-in for the symbol:
+// its device address, which differs per GPU, comes from hipGetSymbolAddress,
+// taken once per device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call per device).
+pkv_status scratch_address(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_API pkv_status paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                             float scale, float* out, const pkv_cache_desc* cache,
+                                             const pkv_decode_opts* opts, void* stream) {
+    pkv_decode_plan plan;
+    pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, opts, &plan);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    st = check_decode(q, k_cache, v_cache, block_tables, context_lens, out);
+    if (st != PKV_OK) return st;
+    if (plan.workspace_bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        st = scratch_address(&ws);
+        if (st != PKV_OK) return st;
+    }
+    return decode_with_workspace(plan, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, num_q_heads, scale, out, ws, cache, opts, stream);
 }
 
 namespace pkv {
@@ -543,6 +616,7 @@ PKV_API const char* pkv_status_string(pkv_status status) {
         case PKV_ERR_ALIGN: return "pointer not 16-byte aligned";
         case PKV_ERR_NO_BLOCKS: return "not enough free blocks in the pool";
         case PKV_ERR_SEQ: return "unknown, repeated or existing sequence id";
+        case PKV_ERR_TOO_LARGE: return "needs more scratch than the allocation-free entry point holds";
     }
     return "unknown status";
 }

@@ -50,7 +50,7 @@ def test_status_strings_and_version(L):
     from paged_kv_cache_276_amd import _lib
 
     assert _lib.status_string(0) == "ok"
-    for s in range(1, 10):
+    for s in range(1, 11):
         assert _lib.status_string(s) not in ("ok", "unknown status")
     assert _lib.status_string(99) == "unknown status"
     assert "gfx950" in L.pkv_version().decode()
@@ -275,3 +275,29 @@ def test_last_launch_info_before_any_call_and_null():
     )
     p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert p.returncode == 0 and p.stdout.strip() == "ok", p.stderr
+
+
+def test_noalloc_rejects_calls_past_its_scratch(L):
+    """The allocation-free decode refuses, before anything is enqueued, a call whose workspace would
+    exceed PKV_NOALLOC_SCRATCH_BYTES (the pointers are never dereferenced: validation fails first);
+    it validates like paged_attn_decode otherwise, and zero sequences enqueue nothing."""
+    import ctypes
+
+    from paged_kv_cache_276_amd import PKV_KERNEL_GENERIC, DecodeOpts, DecodePlan, NOALLOC_SCRATCH_BYTES
+
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never touched
+    desc = _desc(nb=1 << 16, b=16, hkv=8, d=128, dtype=1)
+    plan = DecodePlan()
+    S, Hq, maxb = 4096, 64, 512  # fast workspace: (32768 + 8192) slots x 8 heads x 520 B > 64 MiB
+    assert L.paged_attn_plan(S, Hq, maxb, ctypes.byref(desc), None, ctypes.byref(plan)) == 0
+    assert plan.workspace_bytes > NOALLOC_SCRATCH_BYTES
+    args = (fake, fake, fake, fake, maxb, fake, S, Hq, ctypes.c_float(0.1), fake, ctypes.byref(desc))
+    assert L.paged_attn_decode_noalloc(*args, None, None) == 10
+    small = DecodeOpts(64, PKV_KERNEL_GENERIC, 0, 0)  # generic partitions of 64 over 8,192 tokens
+    assert L.paged_attn_plan(S, Hq, maxb, ctypes.byref(desc), ctypes.byref(small), ctypes.byref(plan)) == 0
+    assert plan.workspace_bytes > NOALLOC_SCRATCH_BYTES
+    assert L.paged_attn_decode_noalloc(*args, ctypes.byref(small), None) == 10
+    null_args = (None, fake, fake, fake, maxb, fake, 4, 8, ctypes.c_float(0.1), fake, ctypes.byref(desc))
+    assert L.paged_attn_decode_noalloc(*null_args, None, None) == 1
+    assert L.paged_attn_decode_noalloc(fake, fake, fake, fake, maxb, fake, 0, 8, ctypes.c_float(0.1), fake,
+                                       ctypes.byref(desc), None, None) == 0
