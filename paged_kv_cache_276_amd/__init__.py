@@ -25,6 +25,7 @@ bf16); ``q`` ``[num_seqs][num_q_heads][head_dim]`` of the pool dtype;
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Dict, Optional, Tuple
 
 import torch
@@ -114,9 +115,32 @@ def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
+def debug_enabled() -> bool:
+    """PKV_DEBUG=1 in the environment turns on the binding's host-side content checks."""
+    return os.environ.get("PKV_DEBUG", "") not in ("", "0")
+
+
+def check_distinct_slots(slots) -> None:
+    """Raise ValueError if two tokens name the same slot (negative slots are skipped, so they may
+    repeat).  Two writes to one slot race in the kernel; the library does not check device
+    contents, so this runs on a host copy when PKV_DEBUG is set."""
+    import numpy as np
+
+    s = np.asarray(slots).astype(np.int64).ravel()
+    s = s[s >= 0]
+    uniq, counts = np.unique(s, return_counts=True)
+    if np.any(counts > 1):
+        dup = uniq[counts > 1]
+        tokens = np.nonzero(np.isin(np.asarray(slots).ravel(), dup[:1]))[0]
+        raise ValueError(f"slot_mapping names {len(dup)} slot(s) more than once "
+                         f"(slot {int(dup[0])} for tokens {tokens.tolist()})")
+
+
 def paged_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
                    k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
-    """Store token t's K/V rows at slot slot_mapping[t] (negative = skip), bit-exact, in place."""
+    """Store token t's K/V rows at slot slot_mapping[t] (negative = skip), bit-exact, in place.
+    With PKV_DEBUG=1 the slots are first read back and checked to be distinct (a synchronising
+    copy; ValueError on a repeat)."""
     dev = k_cache.device
     for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -128,6 +152,8 @@ def paged_kv_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t.dtype == k_cache.dtype, f"{n} dtype must match the cache")
         _need(tuple(t.shape) == (T, desc.num_kv_heads, desc.head_dim), f"{n} must be [T][Hkv][D]")
+    if debug_enabled():
+        check_distinct_slots(slot_mapping.cpu().numpy())
     st = _lib.lib().paged_kv_write(
         ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
         ctypes.c_void_p(slot_mapping.data_ptr()), T, ctypes.c_void_p(k_cache.data_ptr()),

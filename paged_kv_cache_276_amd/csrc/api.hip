@@ -2,7 +2,9 @@
 // include/pagedkv.h and include/pagedkv_blocks.h).  Host code only: argument validation, the launch plan,
 // and dispatch to the kernels.  Every check runs before anything is enqueued.
 #include <stdint.h>
+#include <string.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "launch.h"
@@ -605,7 +607,12 @@ PKV_API pkv_status paged_attn_decode_multi(const void* q, const void* k_cache, c
 }
 
 PKV_API const char* pkv_status_string(pkv_status status) {
-    switch (status) {
+    // A caller may pass any int: read its bits as one (loading an out-of-range
+    // value as the enum type is undefined behaviour in C++).
+    int code = 0;
+    static_assert(sizeof(code) == sizeof(status), "pkv_status is int-sized");
+    std::memcpy(&code, &status, sizeof(code));
+    switch (code) {
         case PKV_OK: return "ok";
         case PKV_ERR_NULL: return "a required pointer is NULL";
         case PKV_ERR_SHAPE: return "invalid or inconsistent size";

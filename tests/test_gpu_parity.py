@@ -371,3 +371,20 @@ def test_block_size_sweep(B, oracle_impl):
     w = make_config("hc_b256", num_seqs=48, block_size=B)
     for k in _kernels_for(w):
         _check_step(w, oracle_impl, f"blocksize{B}/k{k}", kernel=k)
+
+
+def test_debug_duplicate_slots_refused(monkeypatch):
+    """With PKV_DEBUG=1 the binding reads slot_mapping back and refuses a repeated slot before
+    anything is enqueued (the pool stays as it was); without it the same call is enqueued."""
+    w = make_custom([20, 40, 7], 4, 2, 128, 16, torch.bfloat16, seed=61)
+    d = to_device(w)
+    before = d["k_cache"].clone()
+    sm = d["slot_mapping"].clone()
+    sm[2] = sm[0]
+    monkeypatch.setenv("PKV_DEBUG", "1")
+    with pytest.raises(ValueError, match="more than once"):
+        pkv.paged_kv_write(d["k_new"], d["v_new"], sm, d["k_cache"], d["v_cache"])
+    torch.cuda.synchronize()
+    assert torch.equal(d["k_cache"], before)
+    pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])  # distinct: ok
+    torch.cuda.synchronize()
