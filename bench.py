@@ -143,7 +143,8 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-DECODE_KERNELS = ("decode_prefix_kernel", "decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel")
+DECODE_KERNELS = ("decode_prefix_kernel", "decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel",
+                  "multi_query_kernel", "multi_merge_kernel", "multi_sk_kernel", "multi_sk_merge_kernel")
 
 
 def _counter_rows(run_dir: str):
@@ -444,7 +445,7 @@ def bench_multi(args) -> int:
     plan = pkv.paged_attn_multi_plan(w.num_seqs, TQ, mq, w.num_q_heads, w.max_blocks_per_seq, kc,
                                      chunk_tokens=args.partition_tokens)
     out = torch.empty((TQ, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws = torch.empty((plan["workspace_bytes"] + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    ws = pkv.new_workspace(plan["workspace_bytes"], dev)  # zero-filled (the counter region)
 
     def write():
         pkv.paged_kv_write(kn, vn, sm, kc, vc)
@@ -477,8 +478,10 @@ def bench_multi(args) -> int:
         "config": {"workload": args.config, "num_seqs": w.num_seqs, "new_tokens": TQ, "max_q_len": mq,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "context_tokens": int(ctx.sum()),
-                   "lengths": w.meta.get("lengths"), "chunk_tokens": plan["chunk_tokens"]},
+                   "lengths": w.meta.get("lengths"), "chunk_tokens": plan["chunk_tokens"],
+                   "kernel": "multi", "partition_tokens": plan["chunk_tokens"]},
         "roofline": multi_roofline(flops, kv + qo, att),
+        "algorithmic_bytes": {"kv": kv, "q_out": qo, "total": kv + qo},
         "attention_us": att * 1e6,
         "mfma_TFLOPs": flops / att / 1e12,
         "mfma_frac_of_bf16_peak": flops / att / 2.5e15,
@@ -487,6 +490,9 @@ def bench_multi(args) -> int:
                    "per_launch": "K launches back to back / K"},
     }
     rec["attention_us_per_call"] = per_call_percentiles(attend, min(K, 200))
+    rec["roofline"]["traffic"] = _traffic_for(args, f"{args.config}/multi/T{plan['chunk_tokens']}")
+    if args.copy_calibration_mib > 0:
+        rec["copy_calibration_bytes"] = _calibration_copy(dev, args.copy_calibration_mib)
     if not args.no_parity:
         import oracle
 
@@ -501,6 +507,32 @@ def bench_multi(args) -> int:
     rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _traffic_for(args, key: str):
+    """HBM bytes per launch that rocprofv3 counters measured for this workload and kernel family
+    (profiles/traffic.json), or None when there is none for the current kernel sources."""
+    if not os.path.exists(args.traffic_json):
+        return None
+    with open(args.traffic_json) as f:
+        t = json.load(f)
+    if key in t and t[key].get("source_sha") == _kernel_source_sha():
+        return t[key]["bytes_per_launch"]
+    return None
+
+
+def _calibration_copy(dev, mib: int) -> int:
+    """Three device-to-device copies of `mib` MiB (a copy of known size that scales byte counters)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return n
 
 
 def main(argv=None) -> int:
@@ -555,7 +587,7 @@ def main(argv=None) -> int:
                                    partition_tokens=args.partition_tokens, kernel=args.kernel,
                                    grid_waves=args.grid_waves, xcd_balance=args.xcd_balance)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    ws = torch.empty((max(plan["workspace_bytes"], 16) + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    ws = pkv.new_workspace(plan["workspace_bytes"], dev)
 
     def write():
         pkv.paged_kv_write(d["k_new"], d["v_new"], d["slot_mapping"], d["k_cache"], d["v_cache"])
@@ -589,13 +621,8 @@ def main(argv=None) -> int:
     achieved = moved / (dec_avg * 1e-3) / 1e9
     kv_gbs = nbytes["kv"] / (dec_avg * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            t = json.load(f)
-        key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}" + (f"/B{w.block_size}" if args.block_size else "")
-        if key in t and t[key].get("source_sha") == _kernel_source_sha():
-            traffic = t[key]["bytes_per_launch"]
+    key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}" + (f"/B{w.block_size}" if args.block_size else "")
+    traffic = _traffic_for(args, key)
 
     rec = {
         "metric": METRIC,
@@ -678,16 +705,7 @@ def main(argv=None) -> int:
         del scratch, sink
 
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = n
-        del src, dst
+        rec["copy_calibration_bytes"] = _calibration_copy(dev, args.copy_calibration_mib)
 
     if not args.no_parity:
         import oracle

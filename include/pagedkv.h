@@ -113,6 +113,15 @@ typedef struct pkv_decode_opts {
 /* Upper bound of the fast kernel's wave count (sizes its workspace). */
 #define PKV_MAX_GRID_WAVES 8192
 
+/* Every decode workspace (paged_attn_decode, _prefix, _multi) starts with a
+ * counter region of this many bytes: 65536 uint32 arrival counters that
+ * paged_attn_decode_multi uses to merge a unit's context chunks in the chunk
+ * kernel itself.  They must be zero before a workspace's first use with
+ * paged_attn_decode_multi (zero-fill a workspace when allocating it); every
+ * call leaves them zero once its kernels have completed, and no entry point
+ * writes anything else there, so one workspace can serve all of them in turn. */
+#define PKV_WORKSPACE_COUNTER_BYTES (65536u * 4u)
+
 /* What paged_attn_decode will launch for a given shape (host struct). */
 typedef struct pkv_decode_plan {
     int32_t kernel;           /* PKV_KERNEL_GENERIC or PKV_KERNEL_FAST */
@@ -177,8 +186,10 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   scale         softmax scale (normally 1/sqrt(head_dim))
  *   out           (device) fp32 [num_seqs][num_q_heads][head_dim]
  *   workspace     (device) scratch of at least paged_attn_workspace_bytes bytes,
- *                 16-byte aligned; may be NULL when that size is 0.  Its
- *                 contents need no initialisation and are garbage afterwards.
+ *                 16-byte aligned; may be NULL when that size is 0.  Its first
+ *                 PKV_WORKSPACE_COUNTER_BYTES bytes are a counter region that
+ *                 only paged_attn_decode_multi uses; the rest needs no
+ *                 initialisation and is garbage afterwards.
  *   opts          (host) NULL or settings
  *
  * Work splitting.  The generic kernel cuts every sequence into partitions of
@@ -322,7 +333,11 @@ pkv_status paged_attn_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_
  *   max_q_len    (host) at least every q_len; sizes the grid
  *   out          (device) fp32 [total_q][num_q_heads][head_dim]
  * Everything else as paged_attn_decode; the workspace is
- * paged_attn_multi_plan's (no initialisation needed).
+ * paged_attn_multi_plan's, with its counter region (PKV_WORKSPACE_COUNTER_BYTES)
+ * zero before its first use; the rest needs no initialisation.  When the
+ * counters of all (sequence, KV head, row block) units fit that region, the
+ * last chunk workgroup of a unit to finish merges the unit's chunks (one
+ * kernel); larger batches merge them in a second kernel.
  *
  * Device contents are not validated on the host.  A sequence with
  * q_len > max_q_len or > context_lens[i], or a length past the table, gets NaN

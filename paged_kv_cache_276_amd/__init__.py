@@ -57,6 +57,7 @@ __all__ = [
     "paged_attn_workspace_bytes",
     "cache_desc",
     "last_launch_info",
+    "new_workspace",
     "version",
     "PkvError",
 ]
@@ -209,8 +210,20 @@ def paged_attn_workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_s
 
 
 # One cached workspace per (device, stream): calls on one stream are ordered, so
-# they can share it.
+# they can share it.  It is zero-filled when allocated: its first
+# PKV_WORKSPACE_COUNTER_BYTES are the arrival counters of paged_attn_decode_multi,
+# which must start at zero (every call leaves them so).
 _workspaces: Dict[Tuple[torch.device, int], torch.Tensor] = {}
+
+WORKSPACE_COUNTER_BYTES = 65536 * 4  # PKV_WORKSPACE_COUNTER_BYTES of include/pagedkv.h
+
+
+def new_workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zero-filled workspace of at least `nbytes` bytes, ready when this returns (the fill is
+    synchronised, so the workspace can be used on any stream)."""
+    ws = torch.zeros(max(16, (nbytes + 15) // 16 * 16), dtype=torch.uint8, device=device)
+    torch.cuda.synchronize(device)
+    return ws
 
 
 def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Optional[torch.Tensor]:
@@ -219,7 +232,7 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Optiona
     key = (device, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
 

@@ -36,11 +36,20 @@ pkv_status check_desc(const pkv_cache_desc* c) {
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+// Every workspace starts with the same fixed counter region
+// (PKV_WORKSPACE_COUNTER_BYTES: pkv::kCounterUnits uint32 arrival counters).
+// Only the multi-query chunk kernel uses it; it needs the counters at zero when a
+// call starts and leaves them at zero.  No layout puts other data there,
+// whatever the shape, so one zero-filled workspace can serve calls of any shape
+// and entry point in turn.
+constexpr uint64_t kCounterBytes = PKV_WORKSPACE_COUNTER_BYTES;
+static_assert(kCounterBytes == pkv::kCounterUnits * sizeof(uint32_t), "counter region");
+
 struct WorkspaceLayout {
     uint64_t rec_bytes;  // fast: int2 (first partial slot, partial count) [S][Hkv]
     uint64_t ml_bytes;   // generic: float2 [S][Hq][P]; fast: float2 [slots][G]
     uint64_t acc_bytes;  // generic: float [S][Hq][P][D]; fast: float [slots][G][D]
-    uint64_t total;
+    uint64_t total;      // counter region included
 };
 
 // Generic kernel: one partial per (sequence, query head, partition).
@@ -51,7 +60,7 @@ WorkspaceLayout generic_layout(int32_t num_seqs, int32_t num_q_heads, int32_t ma
     const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_parts;
     w.ml_bytes = align_up(rows * sizeof(float2), 256);
     w.acc_bytes = rows * (uint64_t)head_dim * sizeof(float);
-    w.total = w.ml_bytes + w.acc_bytes;
+    w.total = kCounterBytes + w.ml_bytes + w.acc_bytes;
     return w;
 }
 
@@ -65,7 +74,7 @@ WorkspaceLayout fast_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t grou
     w.rec_bytes = align_up(units * sizeof(int2), 256);
     w.ml_bytes = align_up(slots * (uint64_t)group * sizeof(float2), 256);
     w.acc_bytes = slots * (uint64_t)group * (uint64_t)head_dim * sizeof(float);
-    w.total = w.rec_bytes + w.ml_bytes + w.acc_bytes;
+    w.total = kCounterBytes + w.rec_bytes + w.ml_bytes + w.acc_bytes;
     return w;
 }
 
@@ -198,7 +207,7 @@ pkv_status decode_with_workspace(const pkv_decode_plan& plan, const void* q, con
     const WorkspaceLayout wl =
         plan.kernel == PKV_KERNEL_FAST ? fast_layout(num_seqs, cache->num_kv_heads, group, cache->head_dim)
                                        : generic_layout(num_seqs, num_q_heads, plan.max_partitions, cache->head_dim);
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(workspace) + (wl.total ? kCounterBytes : 0);  // past the counter region
     pkv::DecodeArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -421,7 +430,7 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
     if (!workspace || workspace_bytes < pp.total) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGN;
 
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(workspace) + kCounterBytes;  // past the counter region
     const WorkspaceLayout& wl = pp.fast;
     pkv::DecodeArgs a{};
     a.q = q;
@@ -451,7 +460,7 @@ PKV_API pkv_status paged_attn_decode_prefix(const void* q, const void* k_cache, 
     a.num_groups = num_groups;
     a.prefix_chunk_tiles = pp.chunk_tiles;
     a.prefix_max_chunks = pp.max_chunks;
-    const uint64_t poff = align_up(wl.total, 256);
+    const uint64_t poff = align_up(wl.total - kCounterBytes, 256);
     a.ws_pml = reinterpret_cast<float2*>(ws + poff);
     a.ws_pacc = reinterpret_cast<float*>(ws + poff + pp.pml_bytes);
     const hipError_t e = pkv::launch_decode_prefix(a, static_cast<hipStream_t>(stream));
@@ -504,7 +513,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
         w.rec_bytes = align_up(units * sizeof(int2), 256);
         w.ml_bytes = align_up(slots * 16 * sizeof(float2), 256);
         w.acc_bytes = slots * 16 * (uint64_t)cache->head_dim * sizeof(float);
-        w.total = w.rec_bytes + w.ml_bytes + w.acc_bytes;
+        w.total = kCounterBytes + w.rec_bytes + w.ml_bytes + w.acc_bytes;
         mp->chunk_tiles = 0;
         mp->max_chunks = 0;
         mp->pml_bytes = mp->pacc_bytes = 0;
@@ -533,7 +542,7 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     const uint64_t rows = (uint64_t)total_q * num_q_heads * (uint64_t)mc;
     mp->pml_bytes = align_up(rows * sizeof(float2), 256);
     mp->pacc_bytes = rows * (uint64_t)cache->head_dim * sizeof(float);
-    mp->total = mp->pml_bytes + mp->pacc_bytes;
+    mp->total = kCounterBytes + mp->pml_bytes + mp->pacc_bytes;
     mp->base.partition_tokens = (int32_t)ct * 16;
     mp->base.max_partitions = mp->max_chunks;
     mp->base.grid_blocks = (int64_t)num_seqs * cache->num_kv_heads * rb * mc;
@@ -593,6 +602,8 @@ PKV_API pkv_status paged_attn_decode_multi(const void* q, const void* k_cache, c
     a.prefix_chunk_tiles = mp.chunk_tiles;
     a.prefix_max_chunks = mp.max_chunks;
     a.multi_split_runs = mp.split_runs ? 1 : 0;
+    a.ws_cnt = reinterpret_cast<uint32_t*>(ws);  // the counter region
+    ws += kCounterBytes;
     if (mp.split_runs) {
         a.ws_rec = reinterpret_cast<int2*>(ws);
         a.ws_ml = reinterpret_cast<float2*>(ws + mp.runs.rec_bytes);

@@ -85,6 +85,12 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
 
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
+// Device-coherent 64-bit load (another workgroup, maybe on another XCD, stored
+// the value with a device-scope store in this launch).
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int kSegTiles = 128;  // tiles per segment (two per lane in the set-up)
 constexpr uint32_t kFirst = 1u << 16;  // tile 0 of its unit
 constexpr uint32_t kLast = 1u << 17;   // last tile of its unit
@@ -833,6 +839,7 @@ static_assert(kPrefixGroupMax * 8 <= 16 * kPrefixWaves, "rows of a full group at
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+
 template <int BS, int G>
 __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const DecodeArgs a, float qscale) {
     const int tid = threadIdx.x;
@@ -1059,7 +1066,11 @@ struct MultiShape {
     static constexpr int MW = NRG / RG;           // waves per workgroup
 };
 
-template <int BS, int G, int NRG>
+// MERGED: the last workgroup of a (sequence, KV head, row block) to finish its
+// chunk merges all of the unit's chunks (arrival counters in the workspace's
+// counter region, zero between calls) and writes the output rows; without it
+// multi_merge_kernel merges the chunk partials.
+template <int BS, int G, int NRG, bool MERGED>
 __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
     constexpr int RG = MultiShape<NRG>::RG;
     constexpr int MW = MultiShape<NRG>::MW;
@@ -1083,8 +1094,20 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
     const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
     const int ql = q1 - q0;
     const int ctx = a.context_lens[i];
-    // Sequences the merge reports as NaN, and blocks with no rows or tiles (uniform).
-    if (q0 < 0 || q1 > a.total_q || ql < 1 || ql > a.max_q_len || ctx < ql || ctx > table_tokens) return;
+    // Sequences without rows to write, sequences whose rows are NaN (written by
+    // chunk 0 here when merging in-kernel, else by the merge kernel), and blocks
+    // with no rows or tiles (uniform).
+    if (q0 < 0 || q1 > a.total_q || ql < 1) return;
+    if (ql > a.max_q_len || ctx < ql || ctx > table_tokens) {
+        if (MERGED && c == 0) {
+            const int nrow = min(ql, a.max_q_len) * G;
+            for (int r = 16 * NRG * rb; r < min(nrow, 16 * NRG * (rb + 1)); ++r) {
+                float* o = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+                for (int x = tid; x < kHd; x += 64 * MultiShape<NRG>::MW) o[x] = NAN;
+            }
+        }
+        return;
+    }
     const int rows = ql * G;
     const int row0 = 16 * NRG * rb;  // first row of this workgroup
     if (row0 >= rows) return;
@@ -1118,6 +1141,8 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
     const int r16 = lane & 15;
     const int grp = lane >> 4;
     int pos_lim[RG];  // last token the row sees; -1 for a padding row
+    // the smallest of them over the wave's rows (-1 if the wave has a padding row)
+    const int pos_min = wrow0 + 16 * RG <= rows ? ctx - ql + wrow0 / G : -1;
     uint4 qc[RG][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -1212,6 +1237,8 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
     auto step = [&](int j) {
         const int ba = j & 3, bb = (j + 1) & 3;
         const bool has_b = j + 1 < ntile;  // uniform
+        // Every row of the wave sees both tiles whole: no causal selects (uniform).
+        const bool full = has_b && (t0 + j + 2) * kTok - 1 <= pos_min;
         bad |= (tbad_lds[j] | (has_b ? tbad_lds[j + 1] : 0)) != 0;
         f32x4 sa[RG], sb[RG];
 #pragma unroll
@@ -1235,10 +1262,18 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
             const int lim_a = pos_lim[rg] - ((t0 + j) * kTok + 4 * grp);
             const int lim_b = has_b ? lim_a - kTok : -1;
             float s[8];
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s[r] = r <= lim_a ? sa[rg][r] * qscale : -INFINITY;
-                s[4 + r] = r <= lim_b ? sb[rg][r] * qscale : -INFINITY;
+                for (int r = 0; r < 4; ++r) {
+                    s[r] = sa[rg][r] * qscale;
+                    s[4 + r] = sb[rg][r] * qscale;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s[r] = r <= lim_a ? sa[rg][r] * qscale : -INFINITY;
+                    s[4 + r] = r <= lim_b ? sb[rg][r] * qscale : -INFINITY;
+                }
             }
             const float smax =
                 fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
@@ -1259,6 +1294,8 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
             // score is -inf and every weight 0.
             const float mref = m[rg] == -INFINITY ? 0.f : m[rg];
             // p = hi + lo, both bf16: each product with V is exact, the sums fp32.
+            // (p rounded to bf16 alone measured up to 1.6x the tolerance on short
+            // contexts, where few weights carry the output.)
             uint32_t hi[8], lo[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
@@ -1319,24 +1356,157 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
         }
     }
 
-    if (!computes) return;
     const int MC = a.prefix_max_chunks;
+    const int nch = (nt_total + CT - 1) / CT;  // chunks of this sequence
+    float lt[RG];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const float lt = sum_xor32(sum_xor16(l[rg]));
+    for (int rg = 0; rg < RG; ++rg) lt[rg] = computes ? sum_xor32(sum_xor16(l[rg])) : 0.f;
+    // Partial slot of row r (new token r / G, head r % G) for chunk cc.
+    auto prow_of = [&](int r, int cc) -> int64_t { return ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + cc; };
+    if constexpr (!MERGED) {
+        if (!computes) return;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = wrow0 + 16 * rg + 4 * grp + rr;
-            if (r < rows) {
-                const int64_t pr = ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + c;
+        for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
-                for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[rg][jb][rr];
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                if (r < rows) {
+                    const int64_t pr = prow_of(r, c);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[rg][jb][rr];
+                }
             }
+            const int row = wrow0 + 16 * rg + lane;
+            if (lane < 16 && row < rows) a.ws_pml[prow_of(row, c)] = make_float2(m[rg], bad ? NAN : lt[rg]);
         }
-        const int row = wrow0 + 16 * rg + lane;
-        if (lane < 16 && row < rows) {
-            const int64_t pr = ((int64_t)(q0 + row / G) * Hq + (int64_t)g * G + row % G) * MC + c;
-            a.ws_pml[pr] = make_float2(m[rg], bad ? NAN : lt);
+        return;
+    } else {
+        // Rows of the acc layout (rows 4 grp + rr of each group) take the softmax state of
+        // the lane that holds their scores (lane 4 grp + rr).
+        float mr[RG][4], lr[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                mr[rg][rr] = __shfl(m[rg], 4 * grp + rr, kWave);
+                lr[rg][rr] = bad ? NAN : __shfl(lt[rg], 4 * grp + rr, kWave);
+            }
+        __shared__ int last_lds;
+        if (nch > 1) {
+            // Store this chunk's partial past the L2s (another workgroup, maybe on another
+            // XCD, may merge it), make it complete, then count the arrival.
+            if (computes) {
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                        if (r < rows) {
+                            const int64_t pr = prow_of(r, c);
+#pragma unroll
+                            for (int jb = 0; jb < kHd / 16; ++jb)
+                                __hip_atomic_store(&a.ws_pacc[pr * kHd + 16 * jb + r16], acc[rg][jb][rr], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                    const int row = wrow0 + 16 * rg + lane;
+                    if (lane < 16 && row < rows) {
+                        const float2 v = make_float2(m[rg], bad ? NAN : lt[rg]);
+                        __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ws_pml) + prow_of(row, c),
+                                           __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                const int64_t unit = ((int64_t)i * Hkv + g) * rbs + rb;
+                const uint32_t old = __builtin_amdgcn_atomic_inc32(a.ws_cnt + unit, (uint32_t)(nch - 1), __ATOMIC_RELAXED, "agent");
+                last_lds = old == (uint32_t)(nch - 1);
+            }
+            __syncthreads();
+            if (!last_lds) return;  // uniform: a later workgroup merges
+        }
+        if (!computes) return;
+        // The last workgroup (or the only chunk): out = sum_c 2^(m_c - M) acc_c / sum_c
+        // 2^(m_c - M) l_c over the chunks in order, its own from registers.  Chunks a
+        // row cannot see carry m = -inf and weigh nothing.  The loads of one chunk for
+        // all of the lane's rows are issued together.
+        int64_t prw[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                prw[rg][rr] = prow_of(r < rows ? r : wrow0, 0);
+            }
+        const uint64_t* ml64 = reinterpret_cast<const uint64_t*>(a.ws_pml);
+        float M[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) M[rg][rr] = mr[rg][rr];
+        for (int cc = 0; cc < nch; ++cc) {
+            if (cc == c) continue;  // uniform
+            float mc[RG][4];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) mc[rg][rr] = __uint_as_float((uint32_t)load_agent(ml64 + prw[rg][rr] + cc));
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) M[rg][rr] = fmaxf(M[rg][rr], mc[rg][rr]);
+        }
+        // one row group at a time (fewer live registers), the chunks in order
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            float L[4], o[4][kHd / 16];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                L[rr] = 0.f;
+#pragma unroll
+                for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = 0.f;
+            }
+            for (int cc = 0; cc < nch; ++cc) {
+                const bool own = cc == c;  // uniform
+                float mc[4], lc[4], v[4][kHd / 16];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if (own) {
+                        mc[rr] = mr[rg][rr];
+                        lc[rr] = lr[rg][rr];
+#pragma unroll
+                        for (int jb = 0; jb < kHd / 16; ++jb) v[rr][jb] = acc[rg][jb][rr];
+                    } else {
+                        const int64_t pr = prw[rg][rr] + cc;
+                        const uint64_t mlv = load_agent(ml64 + pr);
+                        mc[rr] = __uint_as_float((uint32_t)mlv);
+                        lc[rr] = __uint_as_float((uint32_t)(mlv >> 32));
+#pragma unroll
+                        for (int jb = 0; jb < kHd / 16; ++jb)
+                            v[rr][jb] = __hip_atomic_load(&a.ws_pacc[pr * kHd + 16 * jb + r16], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if (mc[rr] == -INFINITY) continue;
+                    const float wgt = exp2f(mc[rr] - M[rg][rr]);
+                    L[rr] = fmaf(wgt, lc[rr], L[rr]);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = fmaf(wgt, v[rr][jb], o[rr][jb]);
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                if (r < rows) {
+                    float* orow = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) orow[16 * jb + r16] = o[rr][jb] / L[rr];
+                }
+            }
         }
     }
 }
@@ -1830,14 +2000,21 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     const dim3 grid((unsigned)a.num_seqs, (unsigned)(a.num_kv_heads * a.multi_row_blocks), (unsigned)a.prefix_max_chunks);
-    switch (a.multi_waves) {
-        case 1: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1>), grid, dim3(64), 0, stream, a, a.scale * kLog2e); break;
-        case 4: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4>), grid, dim3(256), 0, stream, a, a.scale * kLog2e); break;
-        case 16: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, a.scale * kLog2e); break;
+    // The chunks are merged in the kernel while the arrival counters of all (sequence,
+    // KV head, row block) units fit the workspace's counter region.
+    const bool merged = (int64_t)a.num_seqs * a.num_kv_heads * a.multi_row_blocks <= kCounterUnits;
+    const float qs = a.scale * kLog2e;
+    switch (a.multi_waves * 2 + (merged ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, false>), grid, dim3(64), 0, stream, a, qs); break;
+        case 3: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, true>), grid, dim3(64), 0, stream, a, qs); break;
+        case 8: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, false>), grid, dim3(256), 0, stream, a, qs); break;
+        case 9: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, true>), grid, dim3(256), 0, stream, a, qs); break;
+        case 32: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, false>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
+        case 33: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, true>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || merged) return e;
     hipLaunchKernelGGL((multi_merge_kernel<G>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
     return hipGetLastError();
 }

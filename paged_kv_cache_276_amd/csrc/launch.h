@@ -28,6 +28,7 @@ struct DecodeArgs {
     float* ws_acc;
     float2* ws_ml;
     int2* ws_rec;  // fast kernel: per (seq, kv head) first partial slot and partial count
+    uint32_t* ws_cnt;  // multi-query chunk kernel: arrival counter per (seq, kv head, row block), zero between calls
     int32_t part_tokens;
     int32_t max_parts;
     int32_t grid_waves;  // fast kernel: requested waves (0 = resident capacity)
@@ -52,6 +53,11 @@ struct DecodeArgs {
 };
 
 constexpr int32_t kMaxGridWaves = 8192;  // PKV_MAX_GRID_WAVES
+
+// Every workspace starts with this many uint32 arrival counters
+// (PKV_WORKSPACE_COUNTER_BYTES), used by the multi-query chunk kernel to merge
+// its chunks in-kernel when the batch has at most that many units.
+constexpr int64_t kCounterUnits = 65536;
 
 hipError_t launch_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                            int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_blocks,

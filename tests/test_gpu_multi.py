@@ -179,3 +179,44 @@ def test_multi_split_runs_bad_entry():
             assert torch.isfinite(out[:4]).all() and torch.isfinite(out[8:]).all(), (gw, blk)
             assert torch.allclose(out[:4], good[:4], atol=2e-3, rtol=1e-2)
             assert torch.allclose(out[8:], good[8:], atol=2e-3, rtol=1e-2)
+
+
+def test_multi_chunks_merged_in_kernel_share_a_workspace(oracle_impl):
+    """The chunk kernel merges a unit's chunks itself through the arrival counters at the start of
+    the workspace.  One caller workspace (counter region zero, the rest garbage) serves many-chunk
+    calls (64-token chunks over 3,000-token contexts), a one-chunk call and decode calls in turn;
+    every multi call leaves the counter region zero."""
+    dev = device()
+    ws = torch.full((256 << 20,), 0x5A, dtype=torch.uint8, device=dev)
+    ws[:pkv.WORKSPACE_COUNTER_BYTES].zero_()
+    cases = [
+        (make_multi([3000, 1200, 64], [64, 40, 64], 32, 8, 128, 16, torch.bfloat16, seed=11), 64),
+        (make_multi([500, 77], [20, 16], 8, 2, 128, 32, torch.bfloat16, seed=12), 2048),
+        (make_multi([3000, 1200, 64], [64, 40, 64], 32, 8, 128, 16, torch.bfloat16, seed=11), 128),
+    ]
+    for k, (w, ct) in enumerate(cases):
+        kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+        pkv.paged_kv_write(w.k_new.to(dev), w.v_new.to(dev), torch.from_numpy(w.slot_mapping).to(dev), kc, vc)
+        mq = int(np.max(np.diff(w.cu_q)))
+        args = (w.q.to(dev), kc, vc, torch.from_numpy(w.block_tables).to(dev), torch.from_numpy(w.context_lens).to(dev),
+                torch.from_numpy(w.cu_q).to(dev), mq, w.scale)
+        out = pkv.paged_attn_decode_multi(*args, workspace=ws, chunk_tokens=ct)
+        torch.cuda.synchronize()
+        assert int(ws[:pkv.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, f"case {k}: counters not left at zero"
+        ratio = assert_parity(out, reference(w, oracle_impl)[2], f"shared workspace case {k}")
+        say(f"[gpu] multi shared workspace case {k} (chunk {ct}): ok, err/allowed {ratio:.4f}")
+        # a decode call on the same workspace (its data goes past the counter region)
+        S = w.num_seqs
+        pkv.paged_attn_decode(w.q.to(dev)[w.cu_q[1:] - 1].contiguous(), kc, vc, args[3], args[4], w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:pkv.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "decode wrote into the counter region"
+
+
+def test_multi_chunks_past_the_counter_region(oracle_impl):
+    """More (sequence, KV head, row block) units than the 65,536 counters: the chunk partials are merged
+    by the second kernel instead (8,200 sequences x 8 KV heads, 8 new tokens each, short contexts in
+    chunks of 32 tokens)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    lengths = rng.integers(8, 60, size=8200, endpoint=True).tolist()
+    w = make_multi(lengths, [8] * 8200, 8, 8, 128, 16, torch.bfloat16, seed=13)
+    _check(w, oracle_impl, "past the counter region", chunk_tokens=32)
