@@ -653,6 +653,7 @@ def main(argv=None) -> int:
             "partition_tokens": plan["partition_tokens"],
             "grid_waves": launched["grid"] if launched["kernel"] == "fast" else plan["grid_blocks"],
             "xcd_balance": launched["xcd_balance"] if launched["kernel"] == "fast" else None,
+            "k_loads": (("streamed" if launched["k_stream"] else "cached") if launched["kernel"] == "fast" else None),
         },
         "roofline": {
             "kernel": ("paged_attn_decode_prefix (prefix, suffix and merge kernels, one call; unique bytes)"

@@ -363,6 +363,10 @@ pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const voi
  *                     partition kernel
  *   xcd_balance       fast: the odd-XCD share used, in 64ths (64 = equal); 0 generic
  *   partition_tokens  fast: 16 (tokens per tile); generic: tokens per partition
+ *   k_stream          fast: 1 when K rows were read with non-temporal loads
+ *                     (the units were few and long, at most 1/16 of the
+ *                     resident waves, or the prefix path's suffix pass), 0 when
+ *                     with ordinary loads; V rows are always streamed; 0 generic
  * Per thread and per process; NULL info gives PKV_ERR_NULL.  For callers that
  * check or report the path taken (for example a benchmark).
  */
@@ -371,6 +375,7 @@ typedef struct pkv_launch_info {
     int32_t grid;
     int32_t xcd_balance;
     int32_t partition_tokens;
+    int32_t k_stream;
 } pkv_launch_info;
 pkv_status pkv_last_launch_info(pkv_launch_info *info);
 

@@ -76,7 +76,8 @@ def last_launch_info() -> Dict[str, object]:
     info = _lib.LaunchInfo()
     _lib.check(_lib.lib().pkv_last_launch_info(ctypes.byref(info)), "pkv_last_launch_info")
     return {"kernel": _lib.KERNEL_NAMES.get(info.kernel, "none"), "grid": info.grid,
-            "xcd_balance": info.xcd_balance, "partition_tokens": info.partition_tokens}
+            "xcd_balance": info.xcd_balance, "partition_tokens": info.partition_tokens,
+            "k_stream": bool(info.k_stream)}
 
 
 def cache_desc(k_cache: torch.Tensor) -> CacheDesc:

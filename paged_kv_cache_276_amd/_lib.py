@@ -76,7 +76,7 @@ class DecodePlan(ctypes.Structure):
 
 class LaunchInfo(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("grid", ctypes.c_int32), ("xcd_balance", ctypes.c_int32),
-                ("partition_tokens", ctypes.c_int32)]
+                ("partition_tokens", ctypes.c_int32), ("k_stream", ctypes.c_int32)]
 
 
 class PkvError(RuntimeError):

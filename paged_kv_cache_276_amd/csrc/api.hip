@@ -241,7 +241,7 @@ pkv_status decode_with_workspace(const pkv_decode_plan& plan, const void* q, con
         if (e == hipSuccess && plan.max_partitions > 1) e = pkv::launch_combine(a, s);
         if (e == hipSuccess)
             pkv::last_launch() = pkv::LaunchInfo{PKV_KERNEL_GENERIC, (int32_t)plan.grid_blocks, 0,
-                                                 plan.partition_tokens};
+                                                 plan.partition_tokens, 0};
     }
     return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -321,7 +321,7 @@ PKV_API pkv_status paged_attn_decode_noalloc(const void* q, const void* k_cache,
 
 namespace pkv {
 LaunchInfo& last_launch() {
-    thread_local LaunchInfo info{0, 0, 0, 0};
+    thread_local LaunchInfo info{0, 0, 0, 0, 0};
     return info;
 }
 }  // namespace pkv
@@ -333,6 +333,7 @@ PKV_API pkv_status pkv_last_launch_info(pkv_launch_info* info) {
     info->grid = l.grid;
     info->xcd_balance = l.xcd_balance;
     info->partition_tokens = l.partition_tokens;
+    info->k_stream = l.k_stream;
     return PKV_OK;
 }
 

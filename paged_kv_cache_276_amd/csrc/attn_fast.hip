@@ -76,7 +76,11 @@ struct TileLoad {
 // Loads marked non-temporal: K and V rows are read once per call, and
 // streaming them past the caches' replacement keeps the read rate up
 // (16-byte pieces for the decode kernel, 4-byte ones for the multi-query
-// kernels' LDS-staged tiles; the shared-prefix pass measured no gain).
+// kernels' LDS-staged tiles; the shared-prefix pass measured no gain).  The
+// decode kernel streams V always and K when its units are few and long (see
+// launch_t): with many units, K read with ordinary loads measured faster, and
+// it keeps blocks that several sequences share in the caches.
+__device__ __forceinline__ uint4 load_plain(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -101,7 +105,8 @@ constexpr uint32_t kBad = 1u << 18;    // block-table entry outside the pool
 // START: every sequence i covers tokens [seq_start[i], ctx) only (the tokens
 // before are a shared prefix handled by decode_prefix_kernel), and no unit is
 // finished here: all of them leave partial results for the merge.
-template <int BS, int G, bool START>
+// KSTREAM: K rows read with non-temporal loads too (V rows always are).
+template <int BS, int G, bool START, bool KSTREAM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(const DecodeArgs a,
                                                                                                   float qscale) {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             const int64_t diff = tile2 - (tile_s + (int64_t)BS * kHd);
             const int64_t kx = r16 >= BS ? diff : 0;
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) T.k[kq] = load_stream(kt + koff + kq * 32 + kx);
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = KSTREAM ? load_stream(kt + koff + kq * 32 + kx) : load_plain(kt + koff + kq * 32 + kx);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int vr = min(4 * ii + grp, valid - 1);
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             }
         } else {
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) T.k[kq] = load_stream(kt + koff + kq * 32);
+            for (int kq = 0; kq < 4; ++kq) T.k[kq] = KSTREAM ? load_stream(kt + koff + kq * 32) : load_plain(kt + koff + kq * 32);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const uint32_t voff = (uint32_t)min(4 * ii + grp, valid - 1) * (uint32_t)kHd + (uint32_t)r16 * 8u;
@@ -2036,8 +2041,16 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
         const hipError_t e = launch_prefix_chunks<BS, G>(a, stream);
         if (e != hipSuccess) return e;
     }
-    const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G, PREFIX>);
+    const void* k = reinterpret_cast<const void*>(&decode_fast_kernel<BS, G, PREFIX, true>);
     const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int resident = resident_waves(k);
+    // K rows streamed (non-temporal) when each unit spans many waves (at most a
+    // sixteenth as many units as resident waves), and in the prefix path's suffix
+    // pass; else K is read with ordinary loads.  Same box, alternating: 8 x 32k
+    // 166.4 us streamed against 171.2; 256 sequences of lognormal lengths 271.5
+    // against 276.3, 64 of U[128, 4096] 85.0 against 89.4, and the plain path on
+    // 32 x 8 sequences sharing 2048-token prefixes 302.6 against 368.
+    const bool k_stream = PREFIX || units * 16 <= resident;
     int waves = a.grid_waves;
     bool one_per_simd = false;
     if (waves <= 0) {
@@ -2046,7 +2059,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
         // waves and leave half as many partials.  Measured on one box: 8 x 32k 194.5 ->
         // 190.2 us and 64 sequences of U[128, 4096] 103.2 -> 101.3 us with one per SIMD;
         // 256 sequences (2,048 units) 294.9 against 295.6 us with two.
-        waves = resident_waves(k);
+        waves = resident;
         if (waves >= 16 && units * 4 <= waves) {
             waves = waves / 2 / 8 * 8;
             one_per_simd = true;
@@ -2058,14 +2071,19 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     // 187.5 us against 188.7 at 60/64 and 189.0 at 62/64; 64 sequences: a tie).
     DecodeArgs b = a;
     if (b.xcd_balance == 0) b.xcd_balance = one_per_simd ? 64 : PKV_XCD_BALANCE_DEFAULT;
-    hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX>), dim3(waves), dim3(kWave), 0, stream, b,
-                       b.scale * kLog2e);
+    if (k_stream) {
+        hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX, true>), dim3(waves), dim3(kWave), 0, stream, b,
+                           b.scale * kLog2e);
+    } else if constexpr (!PREFIX) {
+        hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX, false>), dim3(waves), dim3(kWave), 0, stream, b,
+                           b.scale * kLog2e);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((merge_fast_kernel<G, PREFIX>), dim3((unsigned)units), dim3(kWave * G), 0, stream, a,
                        a.max_blocks_per_seq * BS);
     e = hipGetLastError();
-    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, b.xcd_balance, kTok};
+    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, b.xcd_balance, kTok, k_stream ? 1 : 0};
     return e;
 }
 

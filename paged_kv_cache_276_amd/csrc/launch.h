@@ -71,7 +71,7 @@ hipError_t launch_block_copy(void* k_cache, void* v_cache, const int32_t* pairs,
 // The calling thread's last decode launch (kernel family, grid, XCD share,
 // partition tokens), set by the launchers and read by pkv_last_launch_info.
 struct LaunchInfo {
-    int32_t kernel, grid, xcd_balance, partition_tokens;
+    int32_t kernel, grid, xcd_balance, partition_tokens, k_stream;
 };
 LaunchInfo& last_launch();
 

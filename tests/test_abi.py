@@ -267,9 +267,9 @@ def test_last_launch_info_before_any_call_and_null():
         f"sys.path.insert(0, {ROOT!r})\n"
         "from paged_kv_cache_276_amd import _lib\n"
         "L = _lib.lib()\n"
-        "info = _lib.LaunchInfo(7, 7, 7, 7)\n"
+        "info = _lib.LaunchInfo(7, 7, 7, 7, 7)\n"
         "assert L.pkv_last_launch_info(ctypes.byref(info)) == 0\n"
-        "assert (info.kernel, info.grid, info.xcd_balance, info.partition_tokens) == (0, 0, 0, 0)\n"
+        "assert (info.kernel, info.grid, info.xcd_balance, info.partition_tokens, info.k_stream) == (0, 0, 0, 0, 0)\n"
         "assert L.pkv_last_launch_info(None) == 1\n"
         "print('ok')\n"
     )

@@ -162,6 +162,8 @@ def test_launch_info_reports_the_library_choices():
     assert a["kernel"] == b["kernel"] == "fast" and a["partition_tokens"] == 16
     assert a["grid"] % 8 == 0 and b["grid"] == 2 * a["grid"]
     assert a["xcd_balance"] == 64 and b["xcd_balance"] == pkv.XCD_BALANCE_DEFAULT
+    # few long units stream K too; many units read K with ordinary loads (V is always streamed)
+    assert a["k_stream"] and not b["k_stream"]
     run_step(few, kernel=pkv.PKV_KERNEL_FAST, grid_waves=40, xcd_balance=30)
     c = pkv.last_launch_info()
     assert c["grid"] == 40 and c["xcd_balance"] == 30
