@@ -79,7 +79,10 @@ struct TileLoad {
 // kernels' LDS-staged tiles; the shared-prefix pass measured no gain).  The
 // decode kernel streams V always and K when its units are few and long (see
 // launch_t): with many units, K read with ordinary loads measured faster, and
-// it keeps blocks that several sequences share in the caches.
+// it keeps blocks that several sequences share in the caches.  The multi-query
+// chunk kernel reads K with ordinary loads too (121.6 against 126.9 us on
+// 64-token chunks of 16 x 4k); the split-run kernel streams both (121.2
+// against 124.4 us on 4 new tokens x 64 sequences).
 __device__ __forceinline__ uint4 load_plain(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1182,7 +1185,7 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
         const uint32_t* kt = k32 + tile;
         const uint32_t* vt = v32 + tile;
 #pragma unroll
-        for (int k = 0; k < TPI; ++k) t.k[k] = load_stream(kt + lane_off + k * (kHd / 2));
+        for (int k = 0; k < TPI; ++k) t.k[k] = kt[lane_off + k * (kHd / 2)];  // K with ordinary loads: measured faster here
 #pragma unroll
         for (int k = 0; k < TPI; ++k) t.v[k] = load_stream(vt + lane_off + k * (kHd / 2));
     };
