@@ -46,6 +46,7 @@
 
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -1074,12 +1075,183 @@ struct MultiShape {
     static constexpr int MW = NRG / RG;           // waves per workgroup
 };
 
+// The end of a chunk workgroup of the multi-query kernels.  Without MERGED each
+// row leaves the chunk's (m, l, acc) in its partial slot for multi_merge_kernel.
+// With MERGED the last workgroup of a (sequence, KV head, row block) to finish
+// its chunk merges all of the unit's chunks (arrival counters in the
+// workspace's counter region, zero between calls) and writes the output rows.
+template <int G, int RG, bool MERGED>
+__device__ __forceinline__ void multi_finish(const DecodeArgs& a, const f32x4 (&acc)[RG][kHd / 16], const float (&m)[RG],
+                                             const float (&l)[RG], bool bad, bool computes, int i, int g, int rb, int c,
+                                             int q0, int rows, int wrow0, int nt_total, int tid) {
+    const int lane = tid & (kWave - 1);
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const int rbs = a.multi_row_blocks;
+    const int CT = a.prefix_chunk_tiles;
+    const int MC = a.prefix_max_chunks;
+    const int nch = (nt_total + CT - 1) / CT;  // chunks of this sequence
+    float lt[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) lt[rg] = computes ? sum_xor32(sum_xor16(l[rg])) : 0.f;
+    // Partial slot of row r (new token r / G, head r % G) for chunk cc.
+    auto prow_of = [&](int r, int cc) -> int64_t { return ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + cc; };
+    if constexpr (!MERGED) {
+        if (!computes) return;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                if (r < rows) {
+                    const int64_t pr = prow_of(r, c);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[rg][jb][rr];
+                }
+            }
+            const int row = wrow0 + 16 * rg + lane;
+            if (lane < 16 && row < rows) a.ws_pml[prow_of(row, c)] = make_float2(m[rg], bad ? NAN : lt[rg]);
+        }
+        return;
+    } else {
+        // Rows of the acc layout (rows 4 grp + rr of each group) take the softmax state of
+        // the lane that holds their scores (lane 4 grp + rr).
+        float mr[RG][4], lr[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                mr[rg][rr] = __shfl(m[rg], 4 * grp + rr, kWave);
+                lr[rg][rr] = bad ? NAN : __shfl(lt[rg], 4 * grp + rr, kWave);
+            }
+        __shared__ int last_lds;
+        if (nch > 1) {
+            // Store this chunk's partial past the L2s (another workgroup, maybe on another
+            // XCD, may merge it), make it complete, then count the arrival.
+            if (computes) {
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                        if (r < rows) {
+                            const int64_t pr = prow_of(r, c);
+#pragma unroll
+                            for (int jb = 0; jb < kHd / 16; ++jb)
+                                __hip_atomic_store(&a.ws_pacc[pr * kHd + 16 * jb + r16], acc[rg][jb][rr], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                    const int row = wrow0 + 16 * rg + lane;
+                    if (lane < 16 && row < rows) {
+                        const float2 v = make_float2(m[rg], bad ? NAN : lt[rg]);
+                        __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ws_pml) + prow_of(row, c),
+                                           __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                const int64_t unit = ((int64_t)i * Hkv + g) * rbs + rb;
+                const uint32_t old = __builtin_amdgcn_atomic_inc32(a.ws_cnt + unit, (uint32_t)(nch - 1), __ATOMIC_RELAXED, "agent");
+                last_lds = old == (uint32_t)(nch - 1);
+            }
+            __syncthreads();
+            if (!last_lds) return;  // uniform: a later workgroup merges
+        }
+        if (!computes) return;
+        // The last workgroup (or the only chunk): out = sum_c 2^(m_c - M) acc_c / sum_c
+        // 2^(m_c - M) l_c over the chunks in order, its own from registers.  Chunks a
+        // row cannot see carry m = -inf and weigh nothing.  The loads of one chunk for
+        // all of the lane's rows are issued together.
+        int64_t prw[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                prw[rg][rr] = prow_of(r < rows ? r : wrow0, 0);
+            }
+        const uint64_t* ml64 = reinterpret_cast<const uint64_t*>(a.ws_pml);
+        float M[RG][4];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) M[rg][rr] = mr[rg][rr];
+        for (int cc = 0; cc < nch; ++cc) {
+            if (cc == c) continue;  // uniform
+            float mc[RG][4];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) mc[rg][rr] = __uint_as_float((uint32_t)load_agent(ml64 + prw[rg][rr] + cc));
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) M[rg][rr] = fmaxf(M[rg][rr], mc[rg][rr]);
+        }
+        // one row group at a time (fewer live registers), the chunks in order
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            float L[4], o[4][kHd / 16];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                L[rr] = 0.f;
+#pragma unroll
+                for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = 0.f;
+            }
+            for (int cc = 0; cc < nch; ++cc) {
+                const bool own = cc == c;  // uniform
+                float mc[4], lc[4], v[4][kHd / 16];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if (own) {
+                        mc[rr] = mr[rg][rr];
+                        lc[rr] = lr[rg][rr];
+#pragma unroll
+                        for (int jb = 0; jb < kHd / 16; ++jb) v[rr][jb] = acc[rg][jb][rr];
+                    } else {
+                        const int64_t pr = prw[rg][rr] + cc;
+                        const uint64_t mlv = load_agent(ml64 + pr);
+                        mc[rr] = __uint_as_float((uint32_t)mlv);
+                        lc[rr] = __uint_as_float((uint32_t)(mlv >> 32));
+#pragma unroll
+                        for (int jb = 0; jb < kHd / 16; ++jb)
+                            v[rr][jb] = __hip_atomic_load(&a.ws_pacc[pr * kHd + 16 * jb + r16], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    if (mc[rr] == -INFINITY) continue;
+                    const float wgt = exp2f(mc[rr] - M[rg][rr]);
+                    L[rr] = fmaf(wgt, lc[rr], L[rr]);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = fmaf(wgt, v[rr][jb], o[rr][jb]);
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = wrow0 + 16 * rg + 4 * grp + rr;
+                if (r < rows) {
+                    float* orow = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) orow[16 * jb + r16] = o[rr][jb] / L[rr];
+                }
+            }
+        }
+    }
+}
+
 // MERGED: the last workgroup of a (sequence, KV head, row block) to finish its
 // chunk merges all of the unit's chunks (arrival counters in the workspace's
 // counter region, zero between calls) and writes the output rows; without it
 // multi_merge_kernel merges the chunk partials.
 template <int BS, int G, int NRG, bool MERGED>
-__global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(const DecodeArgs a, float qscale) {
+__global__ __launch_bounds__(64 * MultiShape<NRG>::MW) __attribute__((amdgpu_waves_per_eu(NRG == 1 ? 1 : 2))) void multi_query_kernel(
+    const DecodeArgs a, float qscale) {
     constexpr int RG = MultiShape<NRG>::RG;
     constexpr int MW = MultiShape<NRG>::MW;
     constexpr int T = 64 * MW;        // threads
@@ -1364,159 +1536,322 @@ __global__ __launch_bounds__(64 * MultiShape<NRG>::MW) void multi_query_kernel(c
         }
     }
 
-    const int MC = a.prefix_max_chunks;
-    const int nch = (nt_total + CT - 1) / CT;  // chunks of this sequence
-    float lt[RG];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) lt[rg] = computes ? sum_xor32(sum_xor16(l[rg])) : 0.f;
-    // Partial slot of row r (new token r / G, head r % G) for chunk cc.
-    auto prow_of = [&](int r, int cc) -> int64_t { return ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * MC + cc; };
-    if constexpr (!MERGED) {
-        if (!computes) return;
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = wrow0 + 16 * rg + 4 * grp + rr;
-                if (r < rows) {
-                    const int64_t pr = prow_of(r, c);
-#pragma unroll
-                    for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[pr * kHd + 16 * jb + r16] = acc[rg][jb][rr];
-                }
+    multi_finish<G, RG, MERGED>(a, acc, m, l, bad, computes, i, g, rb, c, q0, rows, wrow0, nt_total, tid);
+}
+
+// LDS row of a transposed V pair: one dim, 16 tokens of each of the pair's two
+// tiles (64 bytes), padded to 80.  Chunk c of a row holds tokens 4c .. 4c + 3
+// of the first tile, then the same tokens of the second: the eight k values
+// one lane feeds to the 32-deep P.V product, read as one 16-byte piece.  Rows
+// 20 banks apart put the 16 rows of one read (dims 16 jb .. 16 jb + 15) on 16
+// different 4-bank groups.  The chunks are permuted by bits 4-5 of the row,
+// which one read never spans, so that a tile's stores (each lane its own dim
+// row, 8 bytes) fall at most two lanes to a bank.
+constexpr int kVpRow = 80;
+__device__ __forceinline__ int vp_off(int d, int c) { return d * kVpRow + 16 * (c ^ ((d >> 4) & 3)); }
+
+// max(a, b, c) in one instruction.  Scores come from matrix products, never
+// signalling NaNs, so the quieting that fmaxf adds before each compare is not
+// needed here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// The chunk kernel with the scores one pair ahead: the same workgroups, row
+// groups, causal limits and results as multi_query_kernel (NRG 4 or 16), but
+// each step computes S of pair p + 1 while it turns the scores of pair p into
+// weights and multiplies them into V, so that the matrix products of one part
+// run while the vector ALU works on the other.  K and V of a pair are staged
+// separately: K two pairs ahead of the scores, V one pair ahead of P.V, each
+// in a two-pair LDS ring, with one barrier per step.  A step stores K of pair
+// p + 2 and V of pair p + 1 (loaded two steps before) and issues the loads of
+// K of pair p + 4 and V of pair p + 3.  The score scale is folded into the
+// exponent (p = 2^(s * qscale - m) as one fma) and the running max is taken
+// on the raw scores, so the host passes a finite, non-zero qscale: its sign
+// is moved onto q (negating bf16 is exact).
+template <int BS, int G, int NRG, bool MERGED>
+__global__ __launch_bounds__(64 * MultiShape<NRG>::MW) __attribute__((amdgpu_waves_per_eu(2))) void multi_pipe_kernel(
+    const DecodeArgs a, float qscale) {
+    constexpr int RG = MultiShape<NRG>::RG;
+    constexpr int MW = MultiShape<NRG>::MW;
+    constexpr int T = 64 * MW;             // threads
+    constexpr int TPP = 2 * kTok * 64 / T;  // tokens of one dword column each thread moves per pair
+    static_assert(NRG == 4 || NRG == 16, "row groups per workgroup");
+    static_assert(TPP % 4 == 0 && TPP <= kTok, "each thread moves whole 4-token chunks of one tile");
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar tile and row arithmetic
+    const int i = blockIdx.x;
+    const int rbs = a.multi_row_blocks;
+    const int g = blockIdx.y / rbs, rb = blockIdx.y % rbs;
+    const int c = blockIdx.z;
+    const int Hkv = a.num_kv_heads, Hq = a.num_q_heads;
+    const int maxB = a.max_blocks_per_seq;
+    const int table_tokens = maxB * BS;
+    const int CT = a.prefix_chunk_tiles;
+
+    const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
+    const int ql = q1 - q0;
+    const int ctx = a.context_lens[i];
+    if (q0 < 0 || q1 > a.total_q || ql < 1) return;
+    if (ql > a.max_q_len || ctx < ql || ctx > table_tokens) {
+        if (MERGED && c == 0) {
+            const int nrow = min(ql, a.max_q_len) * G;
+            for (int r = 16 * NRG * rb; r < min(nrow, 16 * NRG * (rb + 1)); ++r) {
+                float* o = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+                for (int x = tid; x < kHd; x += T) o[x] = NAN;
             }
-            const int row = wrow0 + 16 * rg + lane;
-            if (lane < 16 && row < rows) a.ws_pml[prow_of(row, c)] = make_float2(m[rg], bad ? NAN : lt[rg]);
         }
         return;
-    } else {
-        // Rows of the acc layout (rows 4 grp + rr of each group) take the softmax state of
-        // the lane that holds their scores (lane 4 grp + rr).
-        float mr[RG][4], lr[RG][4];
+    }
+    const int rows = ql * G;
+    const int row0 = 16 * NRG * rb;
+    if (row0 >= rows) return;
+    const int nt_total = (ctx + kTok - 1) / kTok;
+    const int t0 = c * CT;
+    const int t1 = min(t0 + CT, nt_total);
+    const int ntile = t1 - t0;
+    if (ntile <= 0) return;
+    const int np = (ntile + 1) / 2;  // pairs; an odd last tile is paired with a masked one
+    const int wrow0 = row0 + 16 * RG * wv;
+    const bool computes = wrow0 < rows;
+
+    __shared__ uint2 toff_lds[kMultiChunkTilesMax];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[4][kTok * kKRow];  // pair p: buffers 2 (p % 2), + 1
+    __shared__ __attribute__((aligned(16))) unsigned char vp_lds[2][kHd * kVpRow];  // pair p: buffer p % 2
+
+    const int32_t* __restrict__ bt = a.block_tables;
+    int badp_any = 0;
+    for (int t = tid; t < ntile; t += T) {  // ntile <= kMultiChunkTilesMax (the plan's chunk limit)
+        const int tok0 = (t0 + t) * kTok;
+        const int phys = bt[(int64_t)i * maxB + tok0 / BS];
+        const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
+        const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * (kHd / 2);
+        toff_lds[t] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
+        badp_any |= badp;
+    }
+    const int r16 = lane & 15;
+    const int grp = lane >> 4;
+    int pos_lim[RG];
+    const int pos_min = wrow0 + 16 * RG <= rows ? ctx - ql + wrow0 / G : -1;
+    const uint32_t qsign = qscale < 0.f ? 0x80008000u : 0u;
+    const float qs = fabsf(qscale);
+    uint4 qc[RG][4];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
+    for (int rg = 0; rg < RG; ++rg) {
+        const int row = wrow0 + 16 * rg + r16;
+        const bool real = row < rows;
+        const int jq = real ? row / G : 0;
+        pos_lim[rg] = real ? ctx - ql + jq : -1;
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(a.q) + ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? row % G : 0)) * kHd;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                mr[rg][rr] = __shfl(m[rg], 4 * grp + rr, kWave);
-                lr[rg][rr] = bad ? NAN : __shfl(lt[rg], 4 * grp + rr, kWave);
-            }
-        __shared__ int last_lds;
-        if (nch > 1) {
-            // Store this chunk's partial past the L2s (another workgroup, maybe on another
-            // XCD, may merge it), make it complete, then count the arrival.
-            if (computes) {
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int r = wrow0 + 16 * rg + 4 * grp + rr;
-                        if (r < rows) {
-                            const int64_t pr = prow_of(r, c);
-#pragma unroll
-                            for (int jb = 0; jb < kHd / 16; ++jb)
-                                __hip_atomic_store(&a.ws_pacc[pr * kHd + 16 * jb + r16], acc[rg][jb][rr], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                    }
-                    const int row = wrow0 + 16 * rg + lane;
-                    if (lane < 16 && row < rows) {
-                        const float2 v = make_float2(m[rg], bad ? NAN : lt[rg]);
-                        __hip_atomic_store(reinterpret_cast<uint64_t*>(a.ws_pml) + prow_of(row, c),
-                                           __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0) {
-                const int64_t unit = ((int64_t)i * Hkv + g) * rbs + rb;
-                const uint32_t old = __builtin_amdgcn_atomic_inc32(a.ws_cnt + unit, (uint32_t)(nch - 1), __ATOMIC_RELAXED, "agent");
-                last_lds = old == (uint32_t)(nch - 1);
-            }
-            __syncthreads();
-            if (!last_lds) return;  // uniform: a later workgroup merges
-        }
-        if (!computes) return;
-        // The last workgroup (or the only chunk): out = sum_c 2^(m_c - M) acc_c / sum_c
-        // 2^(m_c - M) l_c over the chunks in order, its own from registers.  Chunks a
-        // row cannot see carry m = -inf and weigh nothing.  The loads of one chunk for
-        // all of the lane's rows are issued together.
-        int64_t prw[RG][4];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = wrow0 + 16 * rg + 4 * grp + rr;
-                prw[rg][rr] = prow_of(r < rows ? r : wrow0, 0);
-            }
-        const uint64_t* ml64 = reinterpret_cast<const uint64_t*>(a.ws_pml);
-        float M[RG][4];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) M[rg][rr] = mr[rg][rr];
-        for (int cc = 0; cc < nch; ++cc) {
-            if (cc == c) continue;  // uniform
-            float mc[RG][4];
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) mc[rg][rr] = __uint_as_float((uint32_t)load_agent(ml64 + prw[rg][rr] + cc));
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) M[rg][rr] = fmaxf(M[rg][rr], mc[rg][rr]);
-        }
-        // one row group at a time (fewer live registers), the chunks in order
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            float L[4], o[4][kHd / 16];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                L[rr] = 0.f;
-#pragma unroll
-                for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = 0.f;
-            }
-            for (int cc = 0; cc < nch; ++cc) {
-                const bool own = cc == c;  // uniform
-                float mc[4], lc[4], v[4][kHd / 16];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    if (own) {
-                        mc[rr] = mr[rg][rr];
-                        lc[rr] = lr[rg][rr];
-#pragma unroll
-                        for (int jb = 0; jb < kHd / 16; ++jb) v[rr][jb] = acc[rg][jb][rr];
-                    } else {
-                        const int64_t pr = prw[rg][rr] + cc;
-                        const uint64_t mlv = load_agent(ml64 + pr);
-                        mc[rr] = __uint_as_float((uint32_t)mlv);
-                        lc[rr] = __uint_as_float((uint32_t)(mlv >> 32));
-#pragma unroll
-                        for (int jb = 0; jb < kHd / 16; ++jb)
-                            v[rr][jb] = __hip_atomic_load(&a.ws_pacc[pr * kHd + 16 * jb + r16], __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    if (mc[rr] == -INFINITY) continue;
-                    const float wgt = exp2f(mc[rr] - M[rg][rr]);
-                    L[rr] = fmaf(wgt, lc[rr], L[rr]);
-#pragma unroll
-                    for (int jb = 0; jb < kHd / 16; ++jb) o[rr][jb] = fmaf(wgt, v[rr][jb], o[rr][jb]);
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = wrow0 + 16 * rg + 4 * grp + rr;
-                if (r < rows) {
-                    float* orow = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
-#pragma unroll
-                    for (int jb = 0; jb < kHd / 16; ++jb) orow[16 * jb + r16] = o[rr][jb] / L[rr];
-                }
-            }
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
+            qc[rg][kq] = real ? make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign) : make_uint4(0, 0, 0, 0);
         }
     }
+    const bool bad = __syncthreads_or(badp_any) != 0;
+
+    // Wave wv moves tokens ptok .. ptok + TPP - 1 of tile ptile of each pair:
+    // each load instruction reads 256 contiguous bytes of one row.
+    const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
+    const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
+    const int vj = tid & 63;
+    const int ptile = (TPP * wv) / kTok;
+    const int ptok = (TPP * wv) % kTok;
+    const uint32_t lane_off = (uint32_t)ptok * (kHd / 2) + (uint32_t)vj;
+    struct Cols {
+        uint32_t x[TPP];
+    };
+    // Tile indices past the chunk are clamped to its last tile: every path
+    // issues the same loads, and the data is never used unmasked.
+    auto tile_base = [&](int p) -> uint64_t {
+        const uint2 o = toff_lds[min(2 * p + ptile, ntile - 1)];
+        return ((uint64_t)__builtin_amdgcn_readfirstlane(o.y) << 32) | __builtin_amdgcn_readfirstlane(o.x);
+    };
+    auto load_k = [&](int p, Cols& t) {
+        const uint32_t* kt = k32 + tile_base(p);
+#pragma unroll
+        for (int k = 0; k < TPP; ++k) t.x[k] = kt[lane_off + k * (kHd / 2)];
+    };
+    auto load_v = [&](int p, Cols& t) {
+        const uint32_t* vt = v32 + tile_base(p);
+#pragma unroll
+        for (int k = 0; k < TPP; ++k) t.x[k] = load_stream(vt + lane_off + k * (kHd / 2));
+    };
+    auto store_k = [&](int p, const Cols& t) {
+        unsigned char* kb = &k_lds[2 * (p & 1) + ptile][ptok * kKRow + 4 * vj];
+#pragma unroll
+        for (int k = 0; k < TPP; ++k) *reinterpret_cast<uint32_t*>(kb + k * kKRow) = t.x[k];
+    };
+    // Value rows past the context (the tail of the last tile) and all of a
+    // tile past the chunk are stored as zeros: their weights are zero, and
+    // 0 * (whatever the slot holds, NaN included) must not reach the sums.
+    auto store_v = [&](int p, const Cols& t) {
+        const int j = 2 * p + ptile;
+        const int tok = (t0 + j) * kTok + ptok;
+        const int vend = j < ntile ? ctx : 0;
+        uint32_t v[TPP];
+#pragma unroll
+        for (int k = 0; k < TPP; ++k) v[k] = t.x[k];
+        if (tok + TPP > vend) {  // uniform: only the last pair
+#pragma unroll
+            for (int k = 0; k < TPP; ++k) v[k] = tok + k < vend ? v[k] : 0u;
+        }
+        unsigned char* vb = &vp_lds[p & 1][8 * ptile];
+#pragma unroll
+        for (int q4 = 0; q4 < TPP / 4; ++q4) {
+            const int ch = ptok / 4 + q4;
+            const uint32_t* w = v + 4 * q4;
+            const uint2 even = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u), __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+            const uint2 odd = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u), __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+            *reinterpret_cast<uint2*>(vb + vp_off(2 * vj, ch)) = even;
+            *reinterpret_cast<uint2*>(vb + vp_off(2 * vj + 1, ch)) = odd;
+        }
+    };
+    // S^T of pair p for every row group: four 16x16x32 MFMAs per tile.
+    auto scores = [&](int p, f32x4 (&s)[RG][2]) {
+        const unsigned char* ka = &k_lds[2 * (p & 1)][r16 * kKRow + grp * 16];
+        const unsigned char* kb = &k_lds[2 * (p & 1) + 1][r16 * kKRow + grp * 16];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) s[rg][0] = s[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            const uint4 fa = *reinterpret_cast<const uint4*>(ka + kq * 64);
+            const uint4 fb = *reinterpret_cast<const uint4*>(kb + kq * 64);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                s[rg][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa), as_bf16x8(qc[rg][kq]), s[rg][0], 0, 0, 0);
+                s[rg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fb), as_bf16x8(qc[rg][kq]), s[rg][1], 0, 0, 0);
+            }
+        }
+    };
+
+    f32x4 acc[RG][kHd / 16];
+    float m[RG], l[RG], thr[RG], nm[RG];  // running max (scaled), sum, max + lazy margin, -max (0 while -inf)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+        for (int jb = 0; jb < kHd / 16; ++jb) acc[rg][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[rg] = -INFINITY;
+        thr[rg] = -INFINITY;
+        nm[rg] = 0.f;
+        l[rg] = 0.f;
+    }
+
+    // Prologue: K of pairs 0 and 1 and V of pair 0 stored, the ring filled
+    // with K of pairs 2, 3 and V of pairs 1, 2, and S of pair 0.
+    Cols KR[2], VR[2];
+    {
+        Cols k0, k1, v0;
+        load_k(0, k0);
+        load_k(1, k1);
+        load_v(0, v0);
+        load_k(2, KR[0]);
+        load_k(3, KR[1]);
+        load_v(1, VR[0]);
+        load_v(2, VR[1]);
+        store_k(0, k0);
+        store_k(1, k1);
+        store_v(0, v0);
+    }
+    __syncthreads();
+    f32x4 SA[RG][2], SB[RG][2];
+    if (computes) scores(0, SA);
+
+    // Step p: S holds the raw scores of pair p; Sn gets those of pair p + 1.
+    // MASK applies the causal limits to S first: tokens a row cannot see, and
+    // all of a missing second tile, score -inf.  Each loop below runs one
+    // kind, so that no step holds a branch between its matrix products and
+    // the vector work they are meant to overlap.
+    auto step = [&](auto mask_tag, int p, Cols& kr, Cols& vr, f32x4 (&S)[RG][2], f32x4 (&Sn)[RG][2]) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        __syncthreads();  // K of pair p + 1 and V of pair p stored; pair p - 1's buffers free
+        store_k(p + 2, kr);
+        store_v(p + 1, vr);
+        load_k(p + 4, kr);
+        load_v(p + 3, vr);
+        if (!computes) return;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            if constexpr (MASK) {
+                // token r of the first (second) tile is visible when r <= lim_a (lim_b)
+                const int j = 2 * p;
+                const int lim_a = pos_lim[rg] - ((t0 + j) * kTok + 4 * grp);
+                const int lim_b = j + 1 < ntile ? lim_a - kTok : -1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    S[rg][0][r] = r <= lim_a ? S[rg][0][r] : -INFINITY;
+                    S[rg][1][r] = r <= lim_b ? S[rg][1][r] : -INFINITY;
+                }
+            }
+            const float sm = max3f(max3f(S[rg][0][0], S[rg][0][1], S[rg][0][2]), max3f(S[rg][0][3], S[rg][1][0], S[rg][1][1]),
+                                   max3f(S[rg][1][2], S[rg][1][3], S[rg][1][3]));
+            if (__any(sm * qs > thr[rg])) {
+                const float tm = max_xor32(max_xor16(sm)) * qs;
+                const float mn = tm > thr[rg] ? tm : m[rg];
+                const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[rg] - mn);
+                m[rg] = mn;
+                thr[rg] = mn + kLazyRescale;
+                nm[rg] = mn == -INFINITY ? 0.f : -mn;
+                l[rg] *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * grp + r, kWave);
+#pragma unroll
+                    for (int jb = 0; jb < kHd / 16; ++jb) acc[rg][jb][r] *= ar;
+                }
+            }
+        }
+        // S of the next pair, then the weights of this one and P.V.
+        scores(p + 1, Sn);
+        const unsigned char* vb = &vp_lds[p & 1][0];
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            // p = hi + lo, both bf16 (hi the top half of p's bits, lo the rest
+            // rounded down): each product with V is exact, the sums fp32.
+            uint32_t hi[4], lo[4];
+            float pw[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) pw[r] = fast_exp2(fmaf(S[rg][r >> 2][r & 3], qs, nm[rg]));
+            l[rg] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) {
+                const float r0 = pw[r] - __uint_as_float(__float_as_uint(pw[r]) & 0xffff0000u);
+                const float r1 = pw[r + 1] - __uint_as_float(__float_as_uint(pw[r + 1]) & 0xffff0000u);
+                hi[r / 2] = __builtin_amdgcn_perm(__float_as_uint(pw[r + 1]), __float_as_uint(pw[r]), 0x07060302u);
+                lo[r / 2] = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+            }
+            const uint4 phi = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            const uint4 plo = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+            for (int jb = 0; jb < kHd / 16; ++jb) {
+                const uint4 vv = *reinterpret_cast<const uint4*>(vb + vp_off(16 * jb + r16, grp));
+                acc[rg][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi), as_bf16x8(vv), acc[rg][jb], 0, 0, 0);
+                acc[rg][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo), as_bf16x8(vv), acc[rg][jb], 0, 0, 0);
+            }
+        }
+    };
+    // Pairs every row of the wave sees whole (both tiles, no causal limit),
+    // rounded down to even: those steps skip the masks.  Every wave still
+    // runs np steps, one barrier each.
+    const int span = pos_min < 0 ? 0 : max(0, min((pos_min + 1) / kTok - t0, ntile));  // tiles seen whole by every row
+    const int pf = computes ? (span / 2) & ~1 : 0;
+    int p = 0;
+    for (; p + 2 <= pf; p += 2) {
+        step(std::false_type{}, p, KR[0], VR[0], SA, SB);
+        step(std::false_type{}, p + 1, KR[1], VR[1], SB, SA);
+    }
+    for (; p + 2 <= np; p += 2) {
+        step(std::true_type{}, p, KR[0], VR[0], SA, SB);
+        step(std::true_type{}, p + 1, KR[1], VR[1], SB, SA);
+    }
+    if (p < np) step(std::true_type{}, p, KR[0], VR[0], SA, SB);
+
+    multi_finish<G, RG, MERGED>(a, acc, m, l, bad, computes, i, g, rb, c, q0, rows, wrow0, nt_total, tid);
 }
 
 // Merge of the chunk partials of one new token's G heads (wave h = head g*G+h,
@@ -2012,13 +2347,19 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     // KV head, row block) units fit the workspace's counter region.
     const bool merged = (int64_t)a.num_seqs * a.num_kv_heads * a.multi_row_blocks <= kCounterUnits;
     const float qs = a.scale * kLog2e;
-    switch (a.multi_waves * 2 + (merged ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, false>), grid, dim3(64), 0, stream, a, qs); break;
-        case 3: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, true>), grid, dim3(64), 0, stream, a, qs); break;
-        case 8: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, false>), grid, dim3(256), 0, stream, a, qs); break;
-        case 9: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, true>), grid, dim3(256), 0, stream, a, qs); break;
-        case 32: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, false>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
-        case 33: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, true>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
+    // The pipelined kernel folds the scale into the exponent: a finite, non-zero one.
+    const bool pipe = a.multi_waves != 1 && isfinite(qs) && qs != 0.f;
+    switch (a.multi_waves * 4 + (pipe ? 2 : 0) + (merged ? 1 : 0)) {
+        case 4: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, false>), grid, dim3(64), 0, stream, a, qs); break;
+        case 5: hipLaunchKernelGGL((multi_query_kernel<BS, G, 1, true>), grid, dim3(64), 0, stream, a, qs); break;
+        case 16: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, false>), grid, dim3(256), 0, stream, a, qs); break;
+        case 17: hipLaunchKernelGGL((multi_query_kernel<BS, G, 4, true>), grid, dim3(256), 0, stream, a, qs); break;
+        case 18: hipLaunchKernelGGL((multi_pipe_kernel<BS, G, 4, false>), grid, dim3(256), 0, stream, a, qs); break;
+        case 19: hipLaunchKernelGGL((multi_pipe_kernel<BS, G, 4, true>), grid, dim3(256), 0, stream, a, qs); break;
+        case 64: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, false>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
+        case 65: hipLaunchKernelGGL((multi_query_kernel<BS, G, 16, true>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
+        case 66: hipLaunchKernelGGL((multi_pipe_kernel<BS, G, 16, false>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
+        case 67: hipLaunchKernelGGL((multi_pipe_kernel<BS, G, 16, true>), grid, dim3(64 * MultiShape<16>::MW), 0, stream, a, qs); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();

@@ -77,6 +77,20 @@ def test_multi_cases(case, oracle_impl):
         _check(w, oracle_impl, f"case{case}/ct{ct}", chunk_tokens=ct)
 
 
+def test_multi_scale_sign_and_zero(oracle_impl):
+    """The pipelined chunk kernel (rows in groups of 4 or 16 per workgroup) folds the scale into the
+    exponent and moves a negative scale's sign onto q; a zero scale (equal weights over the visible
+    tokens) is run by the other chunk kernel.  Softmax formula: page "x321.org/?p=939", section
+    "First understand what the KV cache is storing"."""
+    wide = make_multi([700, 300, 90], [20, 64, 7], 8, 2, 128, 16, torch.bfloat16, seed=61, pool_fill=0.8)
+    narrow = make_multi([500, 200], [12, 9], 8, 2, 128, 16, torch.bfloat16, seed=62, pool_fill=0.8)
+    for w, what in ((wide, "16 groups"), (narrow, "4 groups")):
+        for s in (-0.09, 0.0, 0.13):
+            w.base.scale = s
+            for ct in (0, 64):
+                _check(w, oracle_impl, f"{what}, scale {s}/ct{ct}", chunk_tokens=ct)
+
+
 def test_one_new_token_is_decode(oracle_impl):
     """q_len = 1 everywhere gives paged_attn_decode's result."""
     w = make_multi([50, 700, 33, 1200], [1, 1, 1, 1], 8, 2, 128, 16, torch.bfloat16, seed=9)
