@@ -870,7 +870,12 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
     const int t1 = min(t0 + CT, nt_total);
     const int ntile = max(t1 - t0, 0);
     const int rows = count * G;
-    const bool computes = 16 * wv < rows;  // wave-uniform
+    // Row groups of 16; a group with fewer than four gives each row group
+    // D = 4 / (row groups) waves, which split its 128 dims (every wave works).
+    const int nrg = (rows + 15) / 16;
+    const int D = nrg == 1 ? 4 : nrg == 2 ? 2 : 1;
+    const int rg = wv / D, dq = wv % D;
+    const bool computes = rg < nrg;  // wave-uniform
 
     __shared__ uint2 toff_lds[kPrefixChunkTilesMax];  // element offset of each tile (lo, hi)
     __shared__ int tbad_lds[kPrefixChunkTilesMax];
@@ -891,7 +896,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
     const int grp = lane >> 4;
     uint4 qc[4];
     {
-        const int r = 16 * wv + r16;
+        const int r = 16 * rg + r16;
         const bool real = r < rows;
         const int mi = first + (real ? r / G : 0);
         const uint16_t* qrow =
@@ -936,9 +941,12 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
         *reinterpret_cast<uint2*>(&vt_lds[buf][vt_off(2 * vj + 1, vtg)]) = odd;
     };
 
-    f32x4 acc[kHd / 16];  // rows 4 grp .. + 3 of the wave, dims 16 jb + r16
+    auto run = [&](auto d_tag) {
+    constexpr int JB = (kHd / 16) / decltype(d_tag)::value;  // 16-dim blocks of this wave: dims 16 (jb0 + jj) + r16
+    const int jb0 = dq * JB;
+    f32x4 acc[JB];  // rows 4 grp .. + 3 of the wave's row group
 #pragma unroll
-    for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < JB; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY;  // running max of row r16 (the same in its four lane groups)
     float l = 0.f;        // this lane's part of row r16's softmax denominator
     bool bad = false;     // a block-table entry outside the pool
@@ -969,7 +977,7 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
             for (int r = 0; r < 4; ++r) {
                 const float ar = __shfl(alpha, 4 * grp + r, kWave);
 #pragma unroll
-                for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
+                for (int jj = 0; jj < JB; ++jj) acc[jj][r] *= ar;
             }
         }
         s16x4 phi, plo;
@@ -982,11 +990,11 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
             plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
         }
 #pragma unroll
-        for (int jb = 0; jb < kHd / 16; ++jb) {
-            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
+        for (int jj = 0; jj < JB; ++jj) {
+            const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * (jb0 + jj) + r16, grp)]);
             const s16x4 vv = __builtin_bit_cast(s16x4, vb);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jb], 0, 0, 0);
+            acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jj], 0, 0, 0);
+            acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vv, acc[jj], 0, 0, 0);
         }
     };
 
@@ -1038,20 +1046,27 @@ __global__ __launch_bounds__(kPrefixThreads) void decode_prefix_kernel(const Dec
     };
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-        const int r = 16 * wv + 4 * grp + rr;
+        const int r = 16 * rg + 4 * grp + rr;
         int64_t prow;
         bool rbad;
         if (row_state(r, prow, rbad)) {
 #pragma unroll
-            for (int jb = 0; jb < kHd / 16; ++jb) a.ws_pacc[(prow * G + r % G) * kHd + 16 * jb + r16] = acc[jb][rr];
+            for (int jj = 0; jj < JB; ++jj) a.ws_pacc[(prow * G + r % G) * kHd + 16 * (jb0 + jj) + r16] = acc[jj][rr];
         }
     }
-    if (lane < 16) {
-        const int r = 16 * wv + lane;
+    if (lane < 16 && dq == 0) {
+        const int r = 16 * rg + lane;
         int64_t prow;
         bool rbad;
         if (row_state(r, prow, rbad)) a.ws_pml[prow * G + r % G] = make_float2(m, rbad ? NAN : lt);
     }
+    };
+    if (D == 4)
+        run(std::integral_constant<int, 4>{});
+    else if (D == 2)
+        run(std::integral_constant<int, 2>{});
+    else
+        run(std::integral_constant<int, 1>{});
 }
 
 // Several new tokens per sequence, causal.  Workgroup (sequence i, KV head g

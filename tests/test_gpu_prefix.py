@@ -77,6 +77,8 @@ CASES = [
     ([300, 310], 2, 2, 16, [(288, [0, 1])]),                                             # G = 1
     ([600] * 5 + [40] * 3, 8, 4, 32, [(576, [0, 1, 2, 3, 4]), (32, [5, 6, 7])]),          # G = 2
     ([4097, 4100, 4200, 5000], 8, 2, 16, [(4096, [0, 1, 2, 3])]),                         # many chunks
+    # G = 8: 8 members (64 rows, one wave per row group) and 5 (40 rows, three row groups)
+    ([900 + 9 * i for i in range(13)], 16, 2, 32, [(864, list(range(8))), (96, list(range(8, 13)))]),
 ]
 
 
