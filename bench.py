@@ -443,7 +443,7 @@ def bench_multi(args) -> int:
     TQ = int(w.cu_q[-1])
     mq = int(np.max(np.diff(w.cu_q)))
     plan = pkv.paged_attn_multi_plan(w.num_seqs, TQ, mq, w.num_q_heads, w.max_blocks_per_seq, kc,
-                                     chunk_tokens=args.partition_tokens)
+                                     chunk_tokens=args.partition_tokens, grid_waves=args.grid_waves)
     out = torch.empty((TQ, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     ws = pkv.new_workspace(plan["workspace_bytes"], dev)  # zero-filled (the counter region)
 
@@ -452,7 +452,7 @@ def bench_multi(args) -> int:
 
     def attend():
         pkv.paged_attn_decode_multi(q, kc, vc, bt, cl, cu, mq, w.scale, out=out, workspace=ws,
-                                    chunk_tokens=args.partition_tokens)
+                                    chunk_tokens=args.partition_tokens, grid_waves=args.grid_waves)
 
     for _ in range(args.warmup):
         write()
