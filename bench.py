@@ -144,7 +144,7 @@ def cpu_model() -> str:
 
 
 DECODE_KERNELS = ("decode_prefix_kernel", "decode_fast_kernel", "merge_fast_kernel", "decode_generic_kernel", "combine_kernel",
-                  "multi_query_kernel", "multi_merge_kernel", "multi_sk_kernel", "multi_sk_merge_kernel")
+                  "multi_query_kernel", "multi_pipe_kernel", "multi_merge_kernel", "multi_sk_kernel", "multi_sk_merge_kernel")
 
 
 def _counter_rows(run_dir: str):
