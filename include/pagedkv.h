@@ -101,8 +101,11 @@ typedef struct pkv_decode_opts {
                                  1 .. 127; 64 = equal shares; 0 = library choice
                                  (PKV_XCD_BALANCE_DEFAULT with two waves per SIMD, equal shares
                                  when the library launches one per SIMD).  Applies when the
-                                 wave count is a multiple of 8 and there are at least as many
-                                 tiles as waves; results do not depend on it. */
+                                 wave count is a multiple of 8 and there are enough tiles for
+                                 every wave to hold one.  With it, when every XCD has an even
+                                 number of waves, the first half of each XCD's waves (in
+                                 dispatch order) take 80/64 of their share and the second half
+                                 48/64.  Results do not depend on it. */
 } pkv_decode_opts;
 
 /* On the MI355X boxes measured, waves on odd-numbered XCDs drained the same reads 4-9% more
@@ -196,7 +199,7 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * plan.partition_tokens tokens and merges them in a second kernel.  The fast
  * kernel lays all (sequence, KV head, 16-token tile) triples end to end and
  * gives each wave of its grid a contiguous run of tiles (equal runs, or runs
- * weighted by the wave's XCD: opts->xcd_balance), so a long sequence spreads
+ * weighted by the wave's XCD and its half of the XCD's waves: opts->xcd_balance), so a long sequence spreads
  * over several waves and many short ones share a wave; a second kernel merges
  * the pieces of each (sequence, KV head).  Either way every piece yields a
  * running max, a softmax denominator and an unnormalised output, merged by a

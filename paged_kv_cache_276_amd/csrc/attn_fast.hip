@@ -8,7 +8,8 @@
 // them for few long units: see launch_t), so the
 // load is balanced whatever the length mix: a long sequence spreads over many
 // waves, many short ones share a wave.  The runs are equal, or weighted by the
-// wave's XCD (odd XCDs read more slowly; Split in tile_math.h).  Each wave
+// wave's XCD (odd XCDs read more slowly) and by its half of the XCD's waves
+// (the first wave of every SIMD drains faster; Split in tile_math.h).  Each wave
 // finds its first tile from the context lengths alone (two passes of a
 // wave-wide prefix sum), so no host synchronisation or planning kernel is
 // needed.

@@ -99,49 +99,66 @@ __device__ __forceinline__ int64_t div_floor(int64_t num, int64_t den) {
 
 // The fast kernel's split of Nt tiles over W waves.  Waves w = x * W8 + j
 // (j < W8) run on XCD x (workgroups are dealt to the eight XCDs in turn), and
-// a wave's share is wt(x) = b on odd x, 128 - b on even x, in 64ths of an
-// equal share.  S(w), the shares of the waves before w, is W8 * base(x) +
-// j * wt(x) with base(x) the shares of one wave of each XCD before x, so
-// S(W) = 64 W, and wave w takes tiles [floor(Nt S(w) / 64 W), floor(Nt
-// S(w + 1) / 64 W)).  W8 = 0 (or b = 64) is the equal split floor(Nt w / W).
+// a wave's share is wt(x) * wh(j) in 4096ths of an equal share: wt(x) = b on
+// odd x, 128 - b on even x, and wh(j) = 64 + d for the first half of the
+// XCD's waves in dispatch order (j < W8 / 2: with two waves per SIMD, the
+// first wave of every SIMD), 64 - d for the second half.  S(w), the shares of
+// the waves before w, is 64 W8 base(x) + wt(x) * (the wh of the XCD's waves
+// before w), with base(x) the wt of one wave of each XCD before x; S(W) =
+// 4096 W, and wave w takes tiles [floor(Nt S(w) / 4096 W), floor(Nt S(w + 1)
+// / 4096 W)).  W8 = 0 is the equal split floor(Nt w / W).
+constexpr int kFirstHalfShare = 16;  // d above, in 64ths
 struct Split {
     int64_t Nt;
     int W;
     int W8;
     int b;
+    int d;
     __device__ __forceinline__ int wt(int x) const { return (x & 1) ? b : 128 - b; }
     __device__ __forceinline__ int64_t base(int x) const {
         return (int64_t)(x >> 1) * 128 + ((x & 1) ? 128 - b : 0);
     }
+    // wh summed over the first j waves of an XCD
+    __device__ __forceinline__ int64_t halves(int j) const {
+        const int H = W8 / 2;
+        return j < H ? (int64_t)j * (64 + d) : (int64_t)H * (64 + d) + (int64_t)(j - H) * (64 - d);
+    }
     __device__ __forceinline__ int64_t S(int w) const {
-        if (W8 == 0) return 64ll * w;
+        if (W8 == 0) return 4096ll * w;
         const int x = w / W8;
-        return (int64_t)W8 * base(x) + (int64_t)(w - x * W8) * wt(x);
+        return 64ll * W8 * base(x) + (int64_t)wt(x) * halves(w - x * W8);
     }
     // First tile of wave w (w = W gives Nt).
-    __device__ __forceinline__ int64_t start(int w) const { return div_floor(Nt * S(w), 64ll * W); }
+    __device__ __forceinline__ int64_t start(int w) const { return div_floor(Nt * S(w), 4096ll * W); }
     // The wave whose tiles include tile t: the last w with start(w) <= t, i.e.
-    // with S(w) <= T = floor(((t + 1) 64 W - 1) / Nt).
+    // with S(w) <= T = floor(((t + 1) 4096 W - 1) / Nt).
     __device__ __forceinline__ int wave_of(int64_t t) const {
-        const int64_t T = div_floor((t + 1) * 64ll * W - 1, Nt);
-        if (W8 == 0) return (int)min<int64_t>(W - 1, T / 64);
+        const int64_t T = div_floor((t + 1) * 4096ll * W - 1, Nt);
+        if (W8 == 0) return (int)min<int64_t>(W - 1, T / 4096);
         int x = 7;
-        while (x > 0 && (int64_t)W8 * base(x) > T) --x;
-        const int64_t j = (T - (int64_t)W8 * base(x)) / wt(x);
+        while (x > 0 && 64ll * W8 * base(x) > T) --x;
+        const int64_t R = T - 64ll * W8 * base(x);  // shares into XCD x
+        const int H = W8 / 2;
+        const int64_t first = (int64_t)wt(x) * H * (64 + d);
+        const int64_t j = R < first ? R / ((int64_t)wt(x) * (64 + d)) : H + (R - first) / ((int64_t)wt(x) * (64 - d));
         return x * W8 + (int)min<int64_t>(W8 - 1, j);
     }
 };
 
-// The split for W of the grid's waves.  XCD shares apply when W is the whole
-// grid, the grid is a whole number of waves per XCD, and the smaller share is
-// still at least one tile (Nt * min(b, 128 - b) >= 64 W): every wave below W
-// then owns a tile, so the waves that touch a unit are consecutive and each
-// leaves a partial result.
+// The split for W of the grid's waves.  The weighted shares apply when W is
+// the whole grid, the grid is a whole number of waves per XCD, and the
+// smallest share is still at least one tile (Nt * min(b, 128 - b) * (64 - d)
+// >= 4096 W): every wave below W then owns a tile, so the waves that touch a
+// unit are consecutive and each leaves a partial result.  The halves apply
+// with the XCD shares (launches of two waves per SIMD) when every XCD has an
+// even number of waves.
 __device__ __forceinline__ Split make_split(int64_t Nt, int W, int grid_waves, int balance) {
     const int lo = balance < 128 - balance ? balance : 128 - balance;
+    const int W8 = grid_waves / 8;
+    const int d = W8 % 2 == 0 ? kFirstHalfShare : 0;
     const bool per_xcd = W == grid_waves && grid_waves % 8 == 0 && balance != 64 && balance > 0 &&
-                         balance < 128 && Nt * lo >= 64ll * W;
-    return Split{Nt, W, per_xcd ? grid_waves / 8 : 0, per_xcd ? balance : 64};
+                         balance < 128 && Nt * lo * (64 - d) >= 4096ll * W;
+    return Split{Nt, W, per_xcd ? W8 : 0, per_xcd ? balance : 64, per_xcd ? d : 0};
 }
 
 __device__ __forceinline__ int tiles_of(int ctx, int table_tokens) {

@@ -88,40 +88,57 @@ def segment_walk(ctx, hkv, block_size, max_blocks, c0, c1, cur, seg_runs):
         seg0 += seg_len
 
 
+FIRST_HALF_SHARE = 16  # tile_math.h kFirstHalfShare
+
+
 class Split:
     """The kernel's work split (tile_math.h, Split and make_split), integer for integer."""
 
     def __init__(self, Nt, W, grid_waves, balance):
         lo = min(balance, 128 - balance)
+        W8 = grid_waves // 8
+        d = FIRST_HALF_SHARE if W8 % 2 == 0 else 0
         per_xcd = (W == grid_waves and grid_waves % 8 == 0 and balance != 64 and 0 < balance < 128
-                   and Nt * lo >= 64 * W)
+                   and Nt * lo * (64 - d) >= 4096 * W)
         self.Nt, self.W = Nt, W
-        self.W8 = grid_waves // 8 if per_xcd else 0
+        self.W8 = W8 if per_xcd else 0
         self.b = balance if per_xcd else 64
+        self.d = d if per_xcd else 0
 
     def wt(self, x):
         return self.b if x & 1 else 128 - self.b
 
+    def wh(self, j):
+        return 64 + self.d if j < self.W8 // 2 else 64 - self.d
+
     def base(self, x):
         return (x >> 1) * 128 + ((128 - self.b) if x & 1 else 0)
 
+    def halves(self, j):
+        H = self.W8 // 2
+        return j * (64 + self.d) if j < H else H * (64 + self.d) + (j - H) * (64 - self.d)
+
     def S(self, w):
         if self.W8 == 0:
-            return 64 * w
+            return 4096 * w
         x = w // self.W8
-        return self.W8 * self.base(x) + (w - x * self.W8) * self.wt(x)
+        return 64 * self.W8 * self.base(x) + self.wt(x) * self.halves(w - x * self.W8)
 
     def start(self, w):
-        return (self.Nt * self.S(w)) // (64 * self.W)
+        return (self.Nt * self.S(w)) // (4096 * self.W)
 
     def wave_of(self, t):
-        T = ((t + 1) * 64 * self.W - 1) // self.Nt
+        T = ((t + 1) * 4096 * self.W - 1) // self.Nt
         if self.W8 == 0:
-            return min(self.W - 1, T // 64)
+            return min(self.W - 1, T // 4096)
         x = 7
-        while x > 0 and self.W8 * self.base(x) > T:
+        while x > 0 and 64 * self.W8 * self.base(x) > T:
             x -= 1
-        return x * self.W8 + min(self.W8 - 1, (T - self.W8 * self.base(x)) // self.wt(x))
+        R = T - 64 * self.W8 * self.base(x)
+        H = self.W8 // 2
+        first = self.wt(x) * H * (64 + self.d)
+        j = R // (self.wt(x) * (64 + self.d)) if R < first else H + (R - first) // (self.wt(x) * (64 - self.d))
+        return x * self.W8 + min(self.W8 - 1, j)
 
 
 def test_split_inverse_and_nonempty_waves():
@@ -140,9 +157,9 @@ def test_split_inverse_and_nonempty_waves():
             w = sp.wave_of(int(t))
             assert starts[w] <= t < starts[w + 1]
         if sp.W8 and Nt >= 100 * W:  # shares come out as asked, to within a tile
-            for w in (0, sp.W8, 2 * sp.W8 + 1, 3 * sp.W8):
+            for w in (0, sp.W8, 2 * sp.W8 + 1, 3 * sp.W8, sp.W8 - 1, sp.W8 // 2, 5 * sp.W8 + sp.W8 // 2 - 1):
                 x = w // sp.W8
-                want = Nt * sp.wt(x) / (64 * W)
+                want = Nt * sp.wt(x) * sp.wh(w - x * sp.W8) / (4096 * W)
                 assert abs((starts[w + 1] - starts[w]) - want) <= 1
     # equal shares reduce to floor(Nt w / W)
     sp = Split(202792, 2048, 2048, 64)
