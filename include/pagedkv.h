@@ -111,7 +111,7 @@ typedef struct pkv_decode_opts {
 /* On the MI355X boxes measured, waves on odd-numbered XCDs drained the same reads 4-9% more
  * slowly than waves on even ones, so an equal split left the odd XCDs finishing last; their
  * waves get this share (in 64ths) by default. */
-#define PKV_XCD_BALANCE_DEFAULT 60
+#define PKV_XCD_BALANCE_DEFAULT 62
 
 /* Upper bound of the fast kernel's wave count (sizes its workspace). */
 #define PKV_MAX_GRID_WAVES 8192

@@ -91,7 +91,7 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
 
 # Default share (in 64ths of an equal share) of the fast kernel's waves on odd-numbered XCDs;
 # the same value as PKV_XCD_BALANCE_DEFAULT in include/pagedkv.h.
-XCD_BALANCE_DEFAULT = 60
+XCD_BALANCE_DEFAULT = 62
 
 
 def _opts(partition_tokens: int, kernel: int, grid_waves: int = 0, xcd_balance: int = 0) -> DecodeOpts:

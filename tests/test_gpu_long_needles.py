@@ -162,7 +162,7 @@ def test_long_context_needles_default_launch(oracle_impl):
 
 def test_long_context_needles_runs_across_segments(oracle_impl):
     """Eight waves: each run holds 8 units of 2,048 tiles, i.e. 128 segments of 128 tiles, and
-    the XCD shares (60/64 on odd XCDs) put the hand-overs mid-unit."""
+    the XCD shares (62/64 on odd XCDs, and the halves of each XCD) put the hand-overs mid-unit."""
     grid = 8
     balance = pkv.XCD_BALANCE_DEFAULT
     waves, segs = _boundary_tiles(grid, balance)
