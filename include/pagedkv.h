@@ -104,8 +104,8 @@ typedef struct pkv_decode_opts {
                                  wave count is a multiple of 8 and there are enough tiles for
                                  every wave to hold one.  With it, when every XCD has an even
                                  number of waves, the first half of each XCD's waves (in
-                                 dispatch order) take 80/64 of their share and the second half
-                                 48/64.  Results do not depend on it. */
+                                 dispatch order) take 84/64 of their share and the second half
+                                 44/64.  Results do not depend on it. */
 } pkv_decode_opts;
 
 /* On the MI355X boxes measured, waves on odd-numbered XCDs drained the same reads 4-9% more

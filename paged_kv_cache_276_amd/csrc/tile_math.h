@@ -107,7 +107,7 @@ __device__ __forceinline__ int64_t div_floor(int64_t num, int64_t den) {
 // before w), with base(x) the wt of one wave of each XCD before x; S(W) =
 // 4096 W, and wave w takes tiles [floor(Nt S(w) / 4096 W), floor(Nt S(w + 1)
 // / 4096 W)).  W8 = 0 is the equal split floor(Nt w / W).
-constexpr int kFirstHalfShare = 16;  // d above, in 64ths
+constexpr int kFirstHalfShare = 20;  // d above, in 64ths
 struct Split {
     int64_t Nt;
     int W;

@@ -88,7 +88,7 @@ def segment_walk(ctx, hkv, block_size, max_blocks, c0, c1, cur, seg_runs):
         seg0 += seg_len
 
 
-FIRST_HALF_SHARE = 16  # tile_math.h kFirstHalfShare
+FIRST_HALF_SHARE = 20  # tile_math.h kFirstHalfShare
 
 
 class Split:
