@@ -80,7 +80,10 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(const DecodeArgs a, 
         for (int h = 0; h < G; ++h) s[h] = 0.f;
         if (valid) {
             const T* kr = kbase + (int64_t)blk * block_stride + (int64_t)(j & bmask) * D;
-#pragma unroll 4
+            // K chunks in flight: 8 (4 measured 5% slower on bf16 d = 128), 4 where
+            // the row has only 8 chunks (bf16 d = 64: 8 spilled at G >= 8).
+            constexpr int KU = D / CH >= 16 ? 8 : 4;
+#pragma unroll KU
             for (int x = 0; x < D; x += CH) {
                 float kf[CH];
                 Chunk16<E>::load(kr + x, kf);
