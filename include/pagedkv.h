@@ -100,7 +100,8 @@ typedef struct pkv_decode_opts {
                                  64ths of an equal share (waves on even XCDs get 128 minus it),
                                  1 .. 127; 64 = equal shares; 0 = library choice
                                  (PKV_XCD_BALANCE_DEFAULT with two waves per SIMD, equal shares
-                                 when the library launches one per SIMD).  Applies when the
+                                 when the library launches one per SIMD and in the suffix pass
+                                 of paged_attn_decode_prefix).  Applies when the
                                  wave count is a multiple of 8 and there are enough tiles for
                                  every wave to hold one.  With it, when every XCD has an even
                                  number of waves, the first half of each XCD's waves (in

@@ -829,7 +829,7 @@ __global__ __launch_bounds__(64 * G) void merge_fast_kernel(const DecodeArgs a, 
 // Each row's (m, l, acc) for chunk c goes to its member's partial slot.
 constexpr int kPrefixWaves = 4;
 constexpr int kPrefixThreads = kPrefixWaves * 64;
-constexpr int kPrefixAhead = 4;           // tiles in flight per workgroup
+constexpr int kPrefixAhead = 6;           // tiles in flight per workgroup
 constexpr int kPrefixChunkTilesMax = 64;  // LDS table size
 constexpr int kMultiChunkTilesMax = 128;  // LDS table size of the multi-query chunk kernel
 constexpr int kKRow = kHd * 2 + 16;       // padded LDS row of a K tile (bytes): conflict-free fragment reads
@@ -2428,9 +2428,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     if (waves <= 0) return hipErrorInvalidValue;
     // The library's XCD shares: with two waves per SIMD, odd XCDs drain more slowly
     // (PKV_XCD_BALANCE_DEFAULT); with one per SIMD, equal shares measured best (8 x 32k:
-    // 187.5 us against 188.7 at 60/64 and 189.0 at 62/64; 64 sequences: a tie).
+    // 187.5 us against 188.7 at 60/64 and 189.0 at 62/64; 64 sequences: a tie), and so
+    // they did for the prefix path's suffix pass, whose runs are short (32 x 8 samples
+    // past 2048-token prefixes: call 113.3-113.8 us against 117.4-117.5).
     DecodeArgs b = a;
-    if (b.xcd_balance == 0) b.xcd_balance = one_per_simd ? 64 : PKV_XCD_BALANCE_DEFAULT;
+    if (b.xcd_balance == 0) b.xcd_balance = (one_per_simd || PREFIX) ? 64 : PKV_XCD_BALANCE_DEFAULT;
     if (k_stream) {
         hipLaunchKernelGGL((decode_fast_kernel<BS, G, PREFIX, true>), dim3(waves), dim3(kWave), 0, stream, b,
                            b.scale * kLog2e);

@@ -36,7 +36,7 @@ def prefix_args(w, dev, split=8):
     return (torch.from_numpy(start).to(dev), torch.from_numpy(g).to(dev), int(start.max(initial=0)))
 
 
-def run_prefix(w, d=None, write=True, chunk_tokens=0, grid_waves=0, split=8, start_override=None):
+def run_prefix(w, d=None, write=True, chunk_tokens=0, grid_waves=0, split=8, start_override=None, xcd_balance=0):
     d = d or to_device(w)
     dev = d["q"].device
     if write:
@@ -47,7 +47,7 @@ def run_prefix(w, d=None, write=True, chunk_tokens=0, grid_waves=0, split=8, sta
         maxp = max(maxp, int(start.max()))
     out = pkv.paged_attn_decode_prefix(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
                                        start, groups, maxp, w.scale, chunk_tokens=chunk_tokens,
-                                       grid_waves=grid_waves)
+                                       grid_waves=grid_waves, xcd_balance=xcd_balance)
     torch.cuda.synchronize()
     return d, out
 
@@ -67,6 +67,10 @@ def test_shared_prefix_workload(oracle_impl):
     w = make_config("shared_prefix")
     for ct in (0, 256, 1024):
         _check(w, oracle_impl, f"shared_prefix/chunk{ct}", chunk_tokens=ct)
+    # the suffix pass takes equal XCD shares unless asked; weighted shares give the same result
+    assert pkv.last_launch_info()["xcd_balance"] == 64
+    _check(w, oracle_impl, "shared_prefix/xcd62", xcd_balance=62)
+    assert pkv.last_launch_info()["xcd_balance"] == 62
 
 
 CASES = [
