@@ -85,7 +85,10 @@ typedef struct pkv_cache_desc {
 #define PKV_KERNEL_AUTO 0    /* library choice */
 #define PKV_KERNEL_GENERIC 1 /* any supported shape and dtype */
 #define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 8, 16, 32 or 64, group size 1, 2, 4 or 8
-                                (block size 8: a 16-token tile reads two blocks) */
+                                (block size 8: a 16-token tile reads two blocks); or group size 16
+                                with block_size 16, 32 or 64 (the split-run kernel of
+                                paged_attn_decode_multi with one query row per sequence: its 16
+                                rows are the 16 heads) */
 
 /* Optional decode settings (host struct; NULL = all defaults). */
 typedef struct pkv_decode_opts {
@@ -202,7 +205,9 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * gives each wave of its grid a contiguous run of tiles (equal runs, or runs
  * weighted by the wave's XCD and its half of the XCD's waves: opts->xcd_balance), so a long sequence spreads
  * over several waves and many short ones share a wave; a second kernel merges
- * the pieces of each (sequence, KV head).  Either way every piece yields a
+ * the pieces of each (sequence, KV head); at group size 16 the runs are equal
+ * and the pieces go through the multi-query path's tile pipeline and merge.
+ * Either way every piece yields a
  * running max, a softmax denominator and an unnormalised output, merged by a
  * log-sum-exp combine.  Results do not depend on the physical placement of
  * blocks (the summation order is fixed by logical token positions, the wave
@@ -244,7 +249,8 @@ pkv_status paged_attn_decode_noalloc(const void *q, const void *k_cache, const v
  * fast kernel's plan with partition_tokens = tokens per prefix chunk,
  * max_partitions = chunks of the longest prefix, workspace_bytes = the
  * workspace paged_attn_decode_prefix needs.  Shapes as PKV_KERNEL_FAST with
- * block_size 16, 32 or 64 (PKV_ERR_UNSUPPORTED otherwise).
+ * block_size 16, 32 or 64 and group size at most 8 (PKV_ERR_UNSUPPORTED
+ * otherwise).
  * opts->partition_tokens, if nonzero, sets the prefix chunk: a multiple of 16,
  * at most 1024.
  */
@@ -299,7 +305,7 @@ pkv_status paged_attn_decode_prefix(const void *q, const void *k_cache, const vo
  * partition_tokens = tokens per context chunk, max_partitions = chunks of the
  * longest table, grid_blocks = workgroups of the chunk kernel,
  * workspace_bytes.  Shapes as PKV_KERNEL_FAST with block_size 16, 32 or 64
- * (PKV_ERR_UNSUPPORTED otherwise).  The rows of a KV head, max_q_len *
+ * and group size at most 8 (PKV_ERR_UNSUPPORTED otherwise).  The rows of a KV head, max_q_len *
  * (num_q_heads / num_kv_heads), go to workgroups of 1, 4 or 16 groups of 16
  * rows (the fewest that hold them, at most 16; 16 groups are 8 waves of two
  * groups each, so grid threads = 64, 256 or 512), in row blocks; at most 65535
@@ -369,7 +375,8 @@ pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const voi
  *   partition_tokens  fast: 16 (tokens per tile); generic: tokens per partition
  *   k_stream          fast: 1 when K rows were read with non-temporal loads
  *                     (the units were few and long, at most 1/16 of the
- *                     resident waves, or the prefix path's suffix pass), 0 when
+ *                     resident waves, the prefix path's suffix pass, or group
+ *                     size 16), 0 when
  *                     with ordinary loads; V rows are always streamed; 0 generic
  * Per thread and per process; NULL info gives PKV_ERR_NULL.  For callers that
  * check or report the path taken (for example a benchmark).

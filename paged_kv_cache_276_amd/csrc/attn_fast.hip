@@ -1966,7 +1966,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
     // Tiles of sequence i < S; none for a description the merge reports as NaN
     // rows or leaves unwritten.
     auto seq_tiles = [&](int i) -> int {
-        const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1], ctx = a.context_lens[i];
+        const int q0 = a.cu_q ? a.cu_q[i] : i, q1 = a.cu_q ? a.cu_q[i + 1] : i + 1, ctx = a.context_lens[i];
         const int64_t ql = (int64_t)q1 - q0;
         const bool ok = q0 >= 0 && q1 <= a.total_q && ql >= 1 && ql <= a.max_q_len && ctx >= ql && ctx <= table_tokens;
         return ok ? (ctx + kTok - 1) / kTok : 0;
@@ -2033,8 +2033,8 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
 
     for (int64_t t = c0; t < c1;) {
         const int len = (int)min<int64_t>((int64_t)(n - b), c1 - t);  // tiles of this piece
-        const int q0 = a.cu_q[i];
-        const int ql = a.cu_q[i + 1] - q0;
+        const int q0 = a.cu_q ? a.cu_q[i] : i;
+        const int ql = a.cu_q ? a.cu_q[i + 1] - q0 : 1;
         const int ctx = a.context_lens[i];
         const int rows = ql * G;
         const bool real = r16 < rows;
@@ -2237,7 +2237,7 @@ __global__ __launch_bounds__(64 * G) void multi_sk_merge_kernel(const DecodeArgs
     const int lane = threadIdx.x & (kWave - 1);
     const int h = threadIdx.x / kWave;
     const int i = blockIdx.x, j = blockIdx.y, g = blockIdx.z;
-    const int q0 = a.cu_q[i], q1 = a.cu_q[i + 1];
+    const int q0 = a.cu_q ? a.cu_q[i] : i, q1 = a.cu_q ? a.cu_q[i + 1] : i + 1;
     const int ctx = a.context_lens[i];
     const int64_t u = (int64_t)i * a.num_kv_heads + g;
     const int2 rec = a.ws_rec[u];  // garbage, and unused, for an invalid sequence
@@ -2245,6 +2245,10 @@ __global__ __launch_bounds__(64 * G) void multi_sk_merge_kernel(const DecodeArgs
     if (q0 < 0 || q1 > a.total_q || ql < 1 || j >= ql) return;  // no row to write
     float2* out = reinterpret_cast<float2*>(
         a.out + ((int64_t)(q0 + j) * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
+    if (!a.cu_q && ctx == 0) {  // decode of an empty sequence
+        *out = make_float2(0.f, 0.f);
+        return;
+    }
     if (ql > a.max_q_len || ctx < ql || ctx > table_tokens) {
         *out = make_float2(NAN, NAN);
         return;
@@ -2384,6 +2388,29 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Decode with 16 query heads per KV head: the split-run kernel of the
+// multi-query path with one query row per sequence (cu_q absent), whose 16
+// rows are the 16 heads, then its merge.  Its partial slots (16 rows each,
+// after one record per unit) are the fast kernel's workspace at G = 16.
+template <int BS>
+hipError_t launch_decode_g16(const DecodeArgs& a, hipStream_t stream) {
+    DecodeArgs b = a;
+    b.cu_q = nullptr;
+    b.total_q = a.num_seqs;
+    b.max_q_len = 1;
+    const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, 16>);
+    const int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
+    if (waves <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((multi_sk_kernel<BS, 16>), dim3(waves), dim3(kWave), 0, stream, b, b.scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid((unsigned)a.num_seqs, 1u, (unsigned)a.num_kv_heads);
+    hipLaunchKernelGGL((multi_sk_merge_kernel<16>), mgrid, dim3(kWave * 16), 0, stream, b, a.max_blocks_per_seq * BS);
+    e = hipGetLastError();
+    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, 64, kTok, 1};
+    return e;
+}
+
 template <int BS>
 hipError_t multi_by_group(const DecodeArgs& a, hipStream_t stream) {
     switch (a.num_q_heads / a.num_kv_heads) {
@@ -2456,6 +2483,9 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
         case 2: return launch_t<BS, 2, PREFIX>(a, stream);
         case 4: return launch_t<BS, 4, PREFIX>(a, stream);
         case 8: return launch_t<BS, 8, PREFIX>(a, stream);
+        case 16:
+            if constexpr (!PREFIX && BS >= kTok) return launch_decode_g16<BS>(a, stream);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -2463,7 +2493,9 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
-    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8;
+    // 16 query heads per KV head run on the multi-query split-run kernel, which
+    // reads whole 16-token tiles of one block
+    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || (group == 16 && block_size >= kTok);
     const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
     return dtype == 1 && head_dim == kHd && b_ok && g_ok;
 }

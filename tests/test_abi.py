@@ -101,11 +101,17 @@ def test_plan_fast_kernel(L):
             assert st == 0 and plan.kernel == 2, (b, g)
             units, slots = 256 * 8, 256 * 8 + 8192
             assert plan.workspace_bytes >= units * 8 + slots * g * (128 * 4 + 8)
-    for desc, hq in ((_desc(d=64), 32), (_desc(dtype=0), 32), (_desc(), 128)):
+    for desc, hq in ((_desc(d=64), 32), (_desc(dtype=0), 32), (_desc(b=8), 128)):
         st, plan = _plan(L, 4, hq, 16, desc)
         assert st == 0 and plan.kernel == 1
         st, plan = _plan(L, 4, hq, 16, desc, kernel=2)
         assert st == 4
+    # 16 query heads per KV head: the split-run kernel (whole 16-token tiles of one block)
+    for b in (16, 32, 64):
+        st, plan = _plan(L, 256, 128, 64, _desc(nb=30000, b=b))
+        assert st == 0 and plan.kernel == 2, b
+        units, slots = 256 * 8, 256 * 8 + 8192
+        assert plan.workspace_bytes >= units * 8 + slots * 16 * (128 * 4 + 8)
     st, plan = _plan(L, 4, 32, 16, _desc(), waves=100)
     assert st == 0 and plan.grid_blocks == 100
     assert _plan(L, 4, 32, 16, _desc(), waves=8193)[0] == 2
@@ -125,6 +131,14 @@ def test_prefix_and_multi_plans_need_whole_tiles(L):
         st = L.paged_attn_multi_plan(64, 256, 4, 32, 64, ctypes.byref(_desc(nb=30000, b=b)),
                                      ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
         assert st == expect, (b, st)
+    # 16 query heads per KV head decode on the split-run kernel, but neither pass takes them
+    plan = DecodePlan()
+    st = L.paged_attn_prefix_plan(64, 128, 64, 8, 256, ctypes.byref(_desc(nb=30000)),
+                                  ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
+    assert st == 4, st
+    st = L.paged_attn_multi_plan(64, 64, 1, 128, 64, ctypes.byref(_desc(nb=30000)),
+                                 ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
+    assert st == 4, st
 
 
 def test_multi_plan_split_runs(L):

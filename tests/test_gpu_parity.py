@@ -267,6 +267,36 @@ def test_bad_device_contents_stay_in_bounds():
             assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
 
 
+G16_CASES = [(32, 2, 16), (64, 4, 32), (16, 1, 64)]  # (Hq, Hkv, B): 16 query heads per KV head
+
+
+@pytest.mark.parametrize("hq,hkv,B", G16_CASES)
+def test_fast_group_size_16(hq, hkv, B, oracle_impl):
+    """bf16, head_dim 128, 16 query heads per KV head: the library runs the multi-query split-run
+    kernel with one query row per sequence (its 16 rows are the 16 heads) and its merge.  Lengths
+    at tile and block edges, an empty sequence and past 4k, at the library's wave count and at 1, 3
+    and 64 waves; one token gives its value row exactly; bad contents poison only their rows."""
+    lengths = [0, 1, 2, 15, 16, 17, 31, 32, 33, 64, 255, 257, 1000, 2048, 4099]
+    w = make_custom(lengths, hq, hkv, 128, B, torch.bfloat16, seed=300 + B + hq, pool_fill=0.7)
+    for waves in (0, 1, 3, 64):
+        out = _check_step(w, oracle_impl, f"g16/Hq{hq}/Hkv{hkv}/B{B}/waves{waves}", grid_waves=waves)
+        info = pkv.last_launch_info()
+        assert info["kernel"] == "fast" and info["xcd_balance"] == 64 and info["k_stream"], info
+        assert waves == 0 or info["grid"] == waves, info
+        o = out.cpu()
+        assert torch.equal(o[0], torch.zeros_like(o[0]))
+        for h in range(hq):
+            assert torch.equal(o[1, h], w.v_new[1, h // 16].float()), (waves, h)
+    bad = make_custom([40, 40, 40, 40], hq, hkv, 128, B, torch.bfloat16, seed=61 + B)
+    bad.block_tables[1, 1 if B < 40 else 0] = bad.num_blocks + 1000  # entry past the pool
+    bad.block_tables[2, 0] = -7                                      # negative entry
+    bad.context_lens[3] = bad.max_blocks_per_seq * B + 1             # length past the table
+    _, out = run_step(bad)
+    o = out.cpu()
+    assert torch.isfinite(o[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
+
+
 def test_block_size_8_tile_halves(oracle_impl):
     """Block size 8: every 16-token tile of the fast kernel reads two blocks.  Lengths at and around
     the half-tile and tile edges match the oracle; a table entry past a sequence's tokens is never
