@@ -85,10 +85,11 @@ typedef struct pkv_cache_desc {
 #define PKV_KERNEL_AUTO 0    /* library choice */
 #define PKV_KERNEL_GENERIC 1 /* any supported shape and dtype */
 #define PKV_KERNEL_FAST 2    /* bf16, head_dim 128, block_size 8, 16, 32 or 64, group size 1, 2, 4 or 8
-                                (block size 8: a 16-token tile reads two blocks); or group size 16
-                                with block_size 16, 32 or 64 (the split-run kernel of
-                                paged_attn_decode_multi with one query row per sequence: its 16
-                                rows are the 16 heads) */
+                                (block size 8: a 16-token tile reads two blocks); or, with
+                                block_size 16, 32 or 64, group size 16 at head_dim 128 and group
+                                size 1 .. 16 at head_dim 64 or 256 (the split-run kernel of
+                                paged_attn_decode_multi with one query row per sequence: its rows
+                                are the group's heads) */
 
 /* Optional decode settings (host struct; NULL = all defaults). */
 typedef struct pkv_decode_opts {
@@ -205,8 +206,9 @@ pkv_status paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * gives each wave of its grid a contiguous run of tiles (equal runs, or runs
  * weighted by the wave's XCD and its half of the XCD's waves: opts->xcd_balance), so a long sequence spreads
  * over several waves and many short ones share a wave; a second kernel merges
- * the pieces of each (sequence, KV head); at group size 16 the runs are equal
- * and the pieces go through the multi-query path's tile pipeline and merge.
+ * the pieces of each (sequence, KV head); at group size 16 and head dims 64
+ * and 256 the runs are equal and the pieces go through the multi-query path's
+ * tile pipeline and merge.
  * Either way every piece yields a
  * running max, a softmax denominator and an unnormalised output, merged by a
  * log-sum-exp combine.  Results do not depend on the physical placement of
@@ -375,8 +377,8 @@ pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const voi
  *   partition_tokens  fast: 16 (tokens per tile); generic: tokens per partition
  *   k_stream          fast: 1 when K rows were read with non-temporal loads
  *                     (the units were few and long, at most 1/16 of the
- *                     resident waves, the prefix path's suffix pass, or group
- *                     size 16), 0 when
+ *                     resident waves, the prefix path's suffix pass, group
+ *                     size 16, or head dim 64 or 256), 0 when
  *                     with ordinary loads; V rows are always streamed; 0 generic
  * Per thread and per process; NULL info gives PKV_ERR_NULL.  For callers that
  * check or report the path taken (for example a benchmark).

@@ -71,9 +71,12 @@ WorkspaceLayout fast_layout(int32_t num_seqs, int32_t num_kv_heads, int32_t grou
     WorkspaceLayout w{0, 0, 0, 0};
     const uint64_t units = (uint64_t)num_seqs * (uint64_t)num_kv_heads;
     const uint64_t slots = units + (uint64_t)pkv::kMaxGridWaves;
+    // rows of a partial slot: the group, or 16 on the split-run kernel (group
+    // size 16, head dims 64 and 256)
+    const uint64_t rows = (head_dim == 128 && group <= 8) ? (uint64_t)group : 16;
     w.rec_bytes = align_up(units * sizeof(int2), 256);
-    w.ml_bytes = align_up(slots * (uint64_t)group * sizeof(float2), 256);
-    w.acc_bytes = slots * (uint64_t)group * (uint64_t)head_dim * sizeof(float);
+    w.ml_bytes = align_up(slots * rows * sizeof(float2), 256);
+    w.acc_bytes = slots * rows * (uint64_t)head_dim * sizeof(float);
     w.total = kCounterBytes + w.rec_bytes + w.ml_bytes + w.acc_bytes;
     return w;
 }
@@ -109,7 +112,8 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_p
     if (opts && (opts->xcd_balance < 0 || opts->xcd_balance > 127)) return PKV_ERR_SHAPE;
 
     if (kernel == PKV_KERNEL_FAST) {
-        if (group == 16 && cache->num_kv_heads > 65535) return PKV_ERR_SHAPE;  // the merge grid's third dimension
+        const bool split = group == 16 || cache->head_dim != 128;  // the split-run kernel
+        if (split && cache->num_kv_heads > 65535) return PKV_ERR_SHAPE;  // its merge grid's third dimension
         plan->kernel = kernel;
         plan->partition_tokens = 16;
         plan->max_partitions = pkv::kMaxGridWaves;
@@ -369,7 +373,8 @@ pkv_status make_prefix_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_b
     pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &pp->base);
     if (st != PKV_OK) return st;
     if (cache->block_size < 16) return PKV_ERR_UNSUPPORTED;  // the prefix pass reads whole 16-token tiles of one block
-    if (num_q_heads / cache->num_kv_heads > pkv::kPrefixGroupMax) return PKV_ERR_UNSUPPORTED;  // up to 8 heads per KV head
+    if (num_q_heads / cache->num_kv_heads > pkv::kPrefixGroupMax || cache->head_dim != 128)
+        return PKV_ERR_UNSUPPORTED;  // up to 8 heads per KV head, head dim 128
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (num_groups < 0 || max_prefix_tokens < 0) return PKV_ERR_SHAPE;
     if ((int64_t)max_prefix_tokens > (int64_t)max_blocks_per_seq * cache->block_size) return PKV_ERR_SHAPE;
@@ -495,7 +500,8 @@ pkv_status make_multi_plan(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
     pkv_status st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &o, &mp->base);
     if (st != PKV_OK) return st;
     if (cache->block_size < 16) return PKV_ERR_UNSUPPORTED;  // the chunk kernel reads whole 16-token tiles of one block
-    if (num_q_heads / cache->num_kv_heads > 8) return PKV_ERR_UNSUPPORTED;  // up to 8 heads per KV head
+    if (num_q_heads / cache->num_kv_heads > 8 || cache->head_dim != 128)
+        return PKV_ERR_UNSUPPORTED;  // up to 8 heads per KV head, head dim 128
     if (opts && opts->kernel != PKV_KERNEL_AUTO && opts->kernel != PKV_KERNEL_FAST) return PKV_ERR_UNSUPPORTED;
     if (total_q < 0 || max_q_len < 1) return PKV_ERR_SHAPE;
     const int32_t group = num_q_heads / cache->num_kv_heads;

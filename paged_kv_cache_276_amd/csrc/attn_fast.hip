@@ -1951,9 +1951,21 @@ __global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a,
 // or each row's (m, l, acc) to partial slot unit + wave; the wave holding the
 // unit's first tile records the first slot and the number of partials (waves
 // from it to the one holding the unit's last tile) for multi_sk_merge_kernel.
-template <int BS, int G>
+// HD: the head dim (128 on the multi-query path; 64 and 256 for decode).
+// DEC: decode, one query row per sequence (row i of sequence i; cu_q unused).
+template <int BS, int G, int HD, bool DEC>
 __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float qscale) {
-    constexpr int kAhead = 3;  // tiles in flight (32 load registers each; 3 measured 3% faster than 2)
+    static_assert(HD == 64 || HD == 128 || HD == 256, "head dim");
+    // Tile loads: a token row of K or V is HD / 2 dwords.  Lane l moves dword
+    // column(s) l % NCL (+ 64) of TPL tokens, tokens TPL (l / NCL) .. + TPL - 1:
+    // each load instruction reads whole rows (HD = 64: two 128-byte rows).
+    constexpr int NC = HD / 2;                // dword columns of a row
+    constexpr int NCL = NC < kWave ? NC : kWave;
+    constexpr int CPL = NC / NCL;             // columns per lane: 1, or 2 at HD = 256
+    constexpr int TPL = kTok * NCL / kWave;   // tokens per lane: 16, or 8 at HD = 64
+    constexpr int KROW = HD * 2 + 16;         // padded LDS row of a K tile (bytes)
+    // tiles in flight (2 CPL TPL load registers each; 3 measured 3% faster than 2 at HD = 128)
+    constexpr int kAhead = HD == 256 ? 2 : 3;
     constexpr int kSegMax = kPrefixChunkTilesMax;
     const int lane = threadIdx.x;
     const int nwaves = gridDim.x;
@@ -1966,7 +1978,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
     // Tiles of sequence i < S; none for a description the merge reports as NaN
     // rows or leaves unwritten.
     auto seq_tiles = [&](int i) -> int {
-        const int q0 = a.cu_q ? a.cu_q[i] : i, q1 = a.cu_q ? a.cu_q[i + 1] : i + 1, ctx = a.context_lens[i];
+        const int q0 = DEC ? i : a.cu_q[i], q1 = DEC ? i + 1 : a.cu_q[i + 1], ctx = a.context_lens[i];
         const int64_t ql = (int64_t)q1 - q0;
         const bool ok = q0 >= 0 && q1 <= a.total_q && ql >= 1 && ql <= a.max_q_len && ctx >= ql && ctx <= table_tokens;
         return ok ? (ctx + kTok - 1) / kTok : 0;
@@ -2017,42 +2029,41 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
 
     __shared__ uint2 toff_lds[kSegMax];
     __shared__ int tbad_lds[kSegMax];
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * kKRow];
-    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][kHd * kVtRow];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kTok * KROW];
+    __shared__ __attribute__((aligned(16))) unsigned char vt_lds[2][HD * kVtRow];
 
     const int32_t* __restrict__ bt = a.block_tables;
     const uint32_t* __restrict__ k32 = static_cast<const uint32_t*>(a.k_cache);
     const uint32_t* __restrict__ v32 = static_cast<const uint32_t*>(a.v_cache);
     const int r16 = lane & 15;  // this lane's row (scores, softmax state) / output column
     const int grp = lane >> 4;
-    // Tile loads: lane l moves dword column l (dims 2l, 2l + 1) of all 16
-    // tokens of K and of V; each load instruction reads one 256-byte row.
+    const int lcol = lane % NCL, ltok = (lane / NCL) * TPL;  // this lane's first column and token
     struct TileKV {
-        uint32_t k[kTok], v[kTok];
+        uint32_t k[CPL][TPL], v[CPL][TPL];
     };
 
     for (int64_t t = c0; t < c1;) {
         const int len = (int)min<int64_t>((int64_t)(n - b), c1 - t);  // tiles of this piece
-        const int q0 = a.cu_q ? a.cu_q[i] : i;
-        const int ql = a.cu_q ? a.cu_q[i + 1] - q0 : 1;
+        const int q0 = DEC ? i : a.cu_q[i];
+        const int ql = DEC ? 1 : a.cu_q[i + 1] - q0;
         const int ctx = a.context_lens[i];
         const int rows = ql * G;
         const bool real = r16 < rows;
         const int jq = real ? r16 / G : 0;
         const int pos = ctx - ql + jq;  // last token row r16 sees
-        uint4 qc[4];
+        uint4 qc[HD / 32];
         {
             const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                                   ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? r16 % G : 0)) * kHd;
+                                   ((int64_t)(q0 + jq) * Hq + (int64_t)g * G + (real ? r16 % G : 0)) * HD;
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq) {
+            for (int kq = 0; kq < HD / 32; ++kq) {
                 const uint4 v = *reinterpret_cast<const uint4*>(qrow + kq * 32 + grp * 8);
                 qc[kq] = real ? v : make_uint4(0, 0, 0, 0);
             }
         }
-        f32x4 acc[kHd / 16];
+        f32x4 acc[HD / 16];
 #pragma unroll
-        for (int jb = 0; jb < kHd / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jb = 0; jb < HD / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY;
         float l = 0.f;
         bool bad = false;
@@ -2063,7 +2074,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
                 const int tok0 = (t0 + lane) * kTok;
                 const int phys = bt[(int64_t)i * maxB + tok0 / BS];
                 const bool badp = (unsigned)phys >= (unsigned)a.num_blocks;
-                const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * kHd;
+                const int64_t off = (((int64_t)(badp ? 0 : phys) * Hkv + g) * BS + tok0 % BS) * HD;
                 toff_lds[lane] = make_uint2((uint32_t)off, (uint32_t)((uint64_t)off >> 32));
                 tbad_lds[lane] = badp;
             }
@@ -2071,38 +2082,72 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
 
             auto load_tile = [&](int j, TileKV& tk) {
                 const uint2 o = toff_lds[j];
-                const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
+                if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
+                    const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) tk.k[k] = load_stream(k32 + off + k * (kHd / 2));
+                    for (int k = 0; k < kTok; ++k) tk.k[0][k] = load_stream(k32 + off + k * (kHd / 2));
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) tk.v[k] = load_stream(v32 + off + k * (kHd / 2));
+                    for (int k = 0; k < kTok; ++k) tk.v[0][k] = load_stream(v32 + off + k * (kHd / 2));
+                } else {
+                    const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + (int64_t)ltok * NC + lcol;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                        for (int k = 0; k < TPL; ++k) tk.k[c][k] = load_stream(k32 + off + k * NC + c * kWave);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                        for (int k = 0; k < TPL; ++k) tk.v[c][k] = load_stream(v32 + off + k * NC + c * kWave);
+                }
             };
             // K rows as stored (padded rows); V transposed, its rows past the
             // context stored as zeros (0 * whatever the slot holds must not
             // reach the sums; the key rows there only give masked scores).
             auto store_tile = [&](int buf, const TileKV& tk, int j) {
-                unsigned char* kb = &k_lds[buf][4 * lane];
+                if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
+                    unsigned char* kb = &k_lds[buf][4 * lane];
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) *reinterpret_cast<uint32_t*>(kb + k * kKRow) = tk.k[k];
-                const int tokb = (t0 + j) * kTok;
-                uint32_t v[kTok];
+                    for (int k = 0; k < kTok; ++k) *reinterpret_cast<uint32_t*>(kb + k * KROW) = tk.k[0][k];
+                    const int tokb = (t0 + j) * kTok;
+                    uint32_t v[kTok];
 #pragma unroll
-                for (int k = 0; k < kTok; ++k) v[k] = tokb + k < ctx ? tk.v[k] : 0u;
+                    for (int k = 0; k < kTok; ++k) v[k] = tokb + k < ctx ? tk.v[0][k] : 0u;
+                    unsigned char* vb = &vt_lds[buf][0];
+#pragma unroll
+                    for (int k = 0; k < kTok; k += 4) {
+                        const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
+                        const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
+                        *reinterpret_cast<uint2*>(vb + vt_off(2 * lane, k >> 2)) = even;
+                        *reinterpret_cast<uint2*>(vb + vt_off(2 * lane + 1, k >> 2)) = odd;
+                    }
+                    return;
+                }
+                const int tokb = (t0 + j) * kTok + ltok;
                 unsigned char* vb = &vt_lds[buf][0];
 #pragma unroll
-                for (int k = 0; k < kTok; k += 4) {
-                    const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
-                    const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
-                    *reinterpret_cast<uint2*>(vb + vt_off(2 * lane, k >> 2)) = even;
-                    *reinterpret_cast<uint2*>(vb + vt_off(2 * lane + 1, k >> 2)) = odd;
+                for (int c = 0; c < CPL; ++c) {
+                    const int col = lcol + c * kWave;
+                    unsigned char* kb = &k_lds[buf][ltok * KROW + 4 * col];
+#pragma unroll
+                    for (int k = 0; k < TPL; ++k) *reinterpret_cast<uint32_t*>(kb + k * KROW) = tk.k[c][k];
+                    uint32_t v[TPL];
+#pragma unroll
+                    for (int k = 0; k < TPL; ++k) v[k] = tokb + k < ctx ? tk.v[c][k] : 0u;
+#pragma unroll
+                    for (int k = 0; k < TPL; k += 4) {
+                        const uint2 even = make_uint2((v[k] & 0xffffu) | (v[k + 1] << 16), (v[k + 2] & 0xffffu) | (v[k + 3] << 16));
+                        const uint2 odd = make_uint2((v[k] >> 16) | (v[k + 1] & 0xffff0000u), (v[k + 2] >> 16) | (v[k + 3] & 0xffff0000u));
+                        *reinterpret_cast<uint2*>(vb + vt_off(2 * col, (ltok + k) >> 2)) = even;
+                        *reinterpret_cast<uint2*>(vb + vt_off(2 * col + 1, (ltok + k) >> 2)) = odd;
+                    }
                 }
             };
             auto step = [&](int buf, int j) {
                 bad = bad || tbad_lds[j] != 0;
                 f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kq = 0; kq < 4; ++kq) {
-                    const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * kKRow + kq * 64 + grp * 16]);
+                for (int kq = 0; kq < HD / 32; ++kq) {
+                    const uint4 kf = *reinterpret_cast<const uint4*>(&k_lds[buf][r16 * KROW + kq * 64 + grp * 16]);
                     sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qc[kq]), sc, 0, 0, 0);
                 }
                 const int tok = (t0 + j) * kTok + 4 * grp;
@@ -2126,7 +2171,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
                     for (int r = 0; r < 4; ++r) {
                         const float ar = __shfl(alpha, 4 * grp + r, kWave);
 #pragma unroll
-                        for (int jb = 0; jb < kHd / 16; ++jb) acc[jb][r] *= ar;
+                        for (int jb = 0; jb < HD / 16; ++jb) acc[jb][r] *= ar;
                     }
                 }
                 s16x4 phi, plo;
@@ -2139,7 +2184,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
                     plo[r] = (short)(__float_as_uint(pr - __uint_as_float(hb)) >> 16);
                 }
 #pragma unroll
-                for (int jb = 0; jb < kHd / 16; ++jb) {
+                for (int jb = 0; jb < HD / 16; ++jb) {
                     const uint2 vb = *reinterpret_cast<const uint2*>(&vt_lds[buf][vt_off(16 * jb + r16, grp)]);
                     const s16x4 vv = __builtin_bit_cast(s16x4, vb);
                     acc[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vv, acc[jb], 0, 0, 0);
@@ -2188,14 +2233,14 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
             const float lr = __shfl(lt, r, kWave);
             if (r < rows) {
                 if (whole) {
-                    float* o = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * kHd;
+                    float* o = a.out + ((int64_t)(q0 + r / G) * Hq + (int64_t)g * G + r % G) * HD;
                     const float inv = bad ? NAN : 1.f / lr;
 #pragma unroll
-                    for (int jb = 0; jb < kHd / 16; ++jb) o[16 * jb + r16] = acc[jb][rr] * inv;
+                    for (int jb = 0; jb < HD / 16; ++jb) o[16 * jb + r16] = acc[jb][rr] * inv;
                 } else {
-                    float* o = a.ws_acc + (slot * 16 + r) * kHd;
+                    float* o = a.ws_acc + (slot * 16 + r) * HD;
 #pragma unroll
-                    for (int jb = 0; jb < kHd / 16; ++jb) o[16 * jb + r16] = acc[jb][rr];
+                    for (int jb = 0; jb < HD / 16; ++jb) o[16 * jb + r16] = acc[jb][rr];
                 }
             }
         }
@@ -2225,62 +2270,105 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
 }
 
 // Merge for multi_sk_kernel: one workgroup per (sequence, new token j, KV
-// head g), one wave per query head h of the group, lanes owning two columns.
-// Units the tile kernel finished (one partial) are left alone; otherwise row
-// r = j * G + h of the unit gets out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p
-// - M) l_p over the unit's partial slots in order (a partial whose tiles all
-// lie past the row's position has m = -inf and weighs nothing).  Invalid
-// sequence descriptions give NaN rows.
-template <int G>
+// head g), one wave per query head h of the group, lanes owning HD / 64
+// adjacent columns.  Units the tile kernel finished (one partial) are left
+// alone; otherwise row r = j * G + h of the unit gets out = sum_p 2^(m_p - M)
+// acc_p / sum_p 2^(m_p - M) l_p over the unit's partial slots in order (a
+// partial whose tiles all lie past the row's position has m = -inf and weighs
+// nothing).  Invalid sequence descriptions give NaN rows; without cu_q (decode:
+// one row per sequence) an empty sequence gives a zero row.
+// N adjacent floats (N = 1, 2, 4) at an address aligned to 4 N bytes, in one access.
+template <int N>
+__device__ __forceinline__ void load_cols(const float* p, float (&v)[N]) {
+    if constexpr (N == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+    } else if constexpr (N == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        v[0] = t.x, v[1] = t.y;
+    } else {
+        v[0] = *p;
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_cols(float* p, const float (&v)[N]) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+        *p = v[0];
+    }
+}
+
+template <int G, int HD, bool DEC>
 __global__ __launch_bounds__(64 * G) void multi_sk_merge_kernel(const DecodeArgs a, int table_tokens) {
     constexpr int kFew = 8;
+    constexpr int VPL = HD / kWave;  // columns per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int h = threadIdx.x / kWave;
     const int i = blockIdx.x, j = blockIdx.y, g = blockIdx.z;
-    const int q0 = a.cu_q ? a.cu_q[i] : i, q1 = a.cu_q ? a.cu_q[i + 1] : i + 1;
+    const int q0 = DEC ? i : a.cu_q[i], q1 = DEC ? i + 1 : a.cu_q[i + 1];
     const int ctx = a.context_lens[i];
     const int64_t u = (int64_t)i * a.num_kv_heads + g;
     const int2 rec = a.ws_rec[u];  // garbage, and unused, for an invalid sequence
     const int64_t ql = (int64_t)q1 - q0;
     if (q0 < 0 || q1 > a.total_q || ql < 1 || j >= ql) return;  // no row to write
-    float2* out = reinterpret_cast<float2*>(
-        a.out + ((int64_t)(q0 + j) * a.num_q_heads + (int64_t)g * G + h) * kHd + 2 * lane);
-    if (!a.cu_q && ctx == 0) {  // decode of an empty sequence
-        *out = make_float2(0.f, 0.f);
+    float* out = a.out + ((int64_t)(q0 + j) * a.num_q_heads + (int64_t)g * G + h) * HD + VPL * lane;
+    auto put = [&](const float (&o)[VPL]) { store_cols<VPL>(out, o); };
+    auto fill = [&](float x) {
+        float o[VPL];
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[e] = x;
+        put(o);
+    };
+    if (DEC && ctx == 0) {  // decode of an empty sequence
+        fill(0.f);
         return;
     }
     if (ql > a.max_q_len || ctx < ql || ctx > table_tokens) {
-        *out = make_float2(NAN, NAN);
+        fill(NAN);
         return;
     }
     if (rec.y == 1) return;  // finished by the tile kernel
     const int64_t slots = (int64_t)a.num_seqs * a.num_kv_heads + kMaxGridWaves;
     if (rec.y < 1 || rec.x < 0 || (int64_t)rec.x + rec.y > slots) {  // never written: refuse to read
-        *out = make_float2(NAN, NAN);
+        fill(NAN);
         return;
     }
     const int np = rec.y;
     const int r = j * G + h;  // < max_q_len * G <= 16
     auto ml_of = [&](int p) -> float2 { return a.ws_ml[((int64_t)rec.x + p) * 16 + r]; };
-    auto acc_of = [&](int p) -> float2 {
-        return *reinterpret_cast<const float2*>(a.ws_acc + (((int64_t)rec.x + p) * 16 + r) * kHd + 2 * lane);
+    auto acc_of = [&](int p, float (&v)[VPL]) {
+        load_cols<VPL>(a.ws_acc + (((int64_t)rec.x + p) * 16 + r) * HD + VPL * lane, v);
     };
+    float o[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) o[e] = 0.f;
     if (np <= kFew) {
         const float2 mlv = lane < np ? ml_of(lane) : make_float2(-INFINITY, 0.f);
-        float2 v[kFew];
+        float v[kFew][VPL];
 #pragma unroll
-        for (int p = 0; p < kFew; ++p) v[p] = p < np ? acc_of(p) : make_float2(0.f, 0.f);
+        for (int p = 0; p < kFew; ++p) {
+            if (p < np) {
+                acc_of(p, v[p]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VPL; ++e) v[p][e] = 0.f;
+            }
+        }
         const float M = wave_max(mlv.x);
         const float wgt = lane < np ? exp2f(mlv.x - M) : 0.f;
         const float L = wave_sum(wgt * mlv.y);
-        float o0 = 0.f, o1 = 0.f;
 #pragma unroll
         for (int p = 0; p < kFew; ++p) {
             const float wp = read_lane(wgt, p);
-            o0 = fmaf(wp, v[p].x, o0);
-            o1 = fmaf(wp, v[p].y, o1);
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) o[e] = fmaf(wp, v[p][e], o[e]);
         }
-        *out = make_float2(o0 / L, o1 / L);
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[e] /= L;
+        put(o);
         return;
     }
     float M = -INFINITY;
@@ -2292,29 +2380,32 @@ __global__ __launch_bounds__(64 * G) void multi_sk_merge_kernel(const DecodeArgs
         L += exp2f(v.x - M) * v.y;
     }
     L = wave_sum(L);
-    float o0 = 0.f, o1 = 0.f;
     int p = 0;
     for (; p + 4 <= np; p += 4) {  // four partials' loads in flight at once
-        float2 v[4], mlv[4];
+        float v[4][VPL];
+        float2 mlv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[k] = acc_of(p + k);
+            acc_of(p + k, v[k]);
             mlv[k] = ml_of(p + k);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float wgt = exp2f(mlv[k].x - M);
-            o0 = fmaf(wgt, v[k].x, o0);
-            o1 = fmaf(wgt, v[k].y, o1);
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) o[e] = fmaf(wgt, v[k][e], o[e]);
         }
     }
     for (; p < np; ++p) {
-        const float2 v = acc_of(p);
+        float v[VPL];
+        acc_of(p, v);
         const float wgt = exp2f(ml_of(p).x - M);
-        o0 = fmaf(wgt, v.x, o0);
-        o1 = fmaf(wgt, v.y, o1);
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) o[e] = fmaf(wgt, v[e], o[e]);
     }
-    *out = make_float2(o0 / L, o1 / L);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) o[e] /= L;
+    put(o);
 }
 
 namespace {
@@ -2353,13 +2444,13 @@ template <int BS, int G>
 hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 mgrid((unsigned)a.num_seqs, (unsigned)a.max_q_len, (unsigned)a.num_kv_heads);
     if (a.multi_split_runs) {
-        const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, G>);
+        const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, G, kHd, false>);
         const int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
         if (waves <= 0) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((multi_sk_kernel<BS, G>), dim3(waves), dim3(kWave), 0, stream, a, a.scale * kLog2e);
+        hipLaunchKernelGGL((multi_sk_kernel<BS, G, kHd, false>), dim3(waves), dim3(kWave), 0, stream, a, a.scale * kLog2e);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((multi_sk_merge_kernel<G>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
+        hipLaunchKernelGGL((multi_sk_merge_kernel<G, kHd, false>), mgrid, dim3(kWave * G), 0, stream, a, a.max_blocks_per_seq * BS);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)a.num_seqs, (unsigned)(a.num_kv_heads * a.multi_row_blocks), (unsigned)a.prefix_max_chunks);
@@ -2388,24 +2479,25 @@ hipError_t launch_multi_t(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Decode with 16 query heads per KV head: the split-run kernel of the
-// multi-query path with one query row per sequence (cu_q absent), whose 16
-// rows are the 16 heads, then its merge.  Its partial slots (16 rows each,
-// after one record per unit) are the fast kernel's workspace at G = 16.
-template <int BS>
-hipError_t launch_decode_g16(const DecodeArgs& a, hipStream_t stream) {
+// Decode on the split-run kernel of the multi-query path, with one query row
+// per sequence (DEC: row i is sequence i's), whose G rows are the G heads, then its merge:
+// the shapes decode_fast_kernel does not hold (16 query heads per KV head, head
+// dims 64 and 256).  Its partial slots (16 rows each, after one record per
+// unit) are the fast workspace of these shapes.
+template <int BS, int G, int HD>
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
     DecodeArgs b = a;
     b.cu_q = nullptr;
     b.total_q = a.num_seqs;
     b.max_q_len = 1;
-    const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, 16>);
+    const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, G, HD, true>);
     const int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
     if (waves <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((multi_sk_kernel<BS, 16>), dim3(waves), dim3(kWave), 0, stream, b, b.scale * kLog2e);
+    hipLaunchKernelGGL((multi_sk_kernel<BS, G, HD, true>), dim3(waves), dim3(kWave), 0, stream, b, b.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid((unsigned)a.num_seqs, 1u, (unsigned)a.num_kv_heads);
-    hipLaunchKernelGGL((multi_sk_merge_kernel<16>), mgrid, dim3(kWave * 16), 0, stream, b, a.max_blocks_per_seq * BS);
+    hipLaunchKernelGGL((multi_sk_merge_kernel<G, HD, true>), mgrid, dim3(kWave * G), 0, stream, b, a.max_blocks_per_seq * BS);
     e = hipGetLastError();
     if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, 64, kTok, 1};
     return e;
@@ -2484,7 +2576,7 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
         case 4: return launch_t<BS, 4, PREFIX>(a, stream);
         case 8: return launch_t<BS, 8, PREFIX>(a, stream);
         case 16:
-            if constexpr (!PREFIX && BS >= kTok) return launch_decode_g16<BS>(a, stream);
+            if constexpr (!PREFIX && BS >= kTok) return launch_decode_split<BS, 16, kHd>(a, stream);
             return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
@@ -2493,19 +2585,48 @@ hipError_t by_group(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool fast_supports(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
-    // 16 query heads per KV head run on the multi-query split-run kernel, which
-    // reads whole 16-token tiles of one block
-    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || (group == 16 && block_size >= kTok);
+    // 16 query heads per KV head and head dims 64 and 256 run on the multi-query
+    // split-run kernel, which reads whole 16-token tiles of one block
+    const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
     const bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
-    return dtype == 1 && head_dim == kHd && b_ok && g_ok;
+    const bool split = group == 16 || head_dim != kHd;
+    const bool d_ok = head_dim == 64 || head_dim == kHd || head_dim == 256;
+    return dtype == 1 && d_ok && b_ok && g_ok && (!split || block_size >= kTok);
+}
+
+// Decode of head dims 64 and 256 (any group size of the fast family).
+template <int BS, int HD>
+hipError_t split_by_group(const DecodeArgs& a, hipStream_t stream) {
+    if constexpr (BS < kTok) {
+        return hipErrorInvalidValue;
+    } else {
+        switch (a.num_q_heads / a.num_kv_heads) {
+            case 1: return launch_decode_split<BS, 1, HD>(a, stream);
+            case 2: return launch_decode_split<BS, 2, HD>(a, stream);
+            case 4: return launch_decode_split<BS, 4, HD>(a, stream);
+            case 8: return launch_decode_split<BS, 8, HD>(a, stream);
+            case 16: return launch_decode_split<BS, 16, HD>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+}
+
+template <int BS>
+hipError_t fast_by_dim(const DecodeArgs& a, hipStream_t stream) {
+    switch (a.head_dim) {
+        case 64: return split_by_group<BS, 64>(a, stream);
+        case kHd: return by_group<BS, false>(a, stream);
+        case 256: return split_by_group<BS, 256>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t stream) {
     switch (a.block_size) {
-        case 8: return by_group<8, false>(a, stream);
-        case 16: return by_group<16, false>(a, stream);
-        case 32: return by_group<32, false>(a, stream);
-        case 64: return by_group<64, false>(a, stream);
+        case 8: return fast_by_dim<8>(a, stream);
+        case 16: return fast_by_dim<16>(a, stream);
+        case 32: return fast_by_dim<32>(a, stream);
+        case 64: return fast_by_dim<64>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -101,17 +101,19 @@ def test_plan_fast_kernel(L):
             assert st == 0 and plan.kernel == 2, (b, g)
             units, slots = 256 * 8, 256 * 8 + 8192
             assert plan.workspace_bytes >= units * 8 + slots * g * (128 * 4 + 8)
-    for desc, hq in ((_desc(d=64), 32), (_desc(dtype=0), 32), (_desc(b=8), 128)):
+    for desc, hq in ((_desc(d=64, b=8), 32), (_desc(dtype=0), 32), (_desc(b=8), 128), (_desc(d=256, b=8), 32)):
         st, plan = _plan(L, 4, hq, 16, desc)
         assert st == 0 and plan.kernel == 1
         st, plan = _plan(L, 4, hq, 16, desc, kernel=2)
         assert st == 4
-    # 16 query heads per KV head: the split-run kernel (whole 16-token tiles of one block)
+    # 16 query heads per KV head, and head dims 64 and 256: the split-run kernel (whole 16-token
+    # tiles of one block, partial slots of 16 rows)
     for b in (16, 32, 64):
-        st, plan = _plan(L, 256, 128, 64, _desc(nb=30000, b=b))
-        assert st == 0 and plan.kernel == 2, b
-        units, slots = 256 * 8, 256 * 8 + 8192
-        assert plan.workspace_bytes >= units * 8 + slots * 16 * (128 * 4 + 8)
+        for d, hq in ((128, 128), (64, 32), (256, 8), (64, 128)):
+            st, plan = _plan(L, 256, hq, 64, _desc(nb=30000, b=b, d=d))
+            assert st == 0 and plan.kernel == 2, (b, d, hq)
+            units, slots = 256 * 8, 256 * 8 + 8192
+            assert plan.workspace_bytes >= units * 8 + slots * 16 * (d * 4 + 8)
     st, plan = _plan(L, 4, 32, 16, _desc(), waves=100)
     assert st == 0 and plan.grid_blocks == 100
     assert _plan(L, 4, 32, 16, _desc(), waves=8193)[0] == 2
@@ -131,8 +133,16 @@ def test_prefix_and_multi_plans_need_whole_tiles(L):
         st = L.paged_attn_multi_plan(64, 256, 4, 32, 64, ctypes.byref(_desc(nb=30000, b=b)),
                                      ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
         assert st == expect, (b, st)
-    # 16 query heads per KV head decode on the split-run kernel, but neither pass takes them
+    # 16 query heads per KV head and head dims 64 / 256 decode on the split-run kernel, but neither
+    # pass takes them
     plan = DecodePlan()
+    for d in (64, 256):
+        st = L.paged_attn_prefix_plan(64, 32, 64, 8, 256, ctypes.byref(_desc(nb=30000, d=d)),
+                                      ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
+        assert st == 4, (d, st)
+        st = L.paged_attn_multi_plan(64, 256, 4, 32, 64, ctypes.byref(_desc(nb=30000, d=d)),
+                                     ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
+        assert st == 4, (d, st)
     st = L.paged_attn_prefix_plan(64, 128, 64, 8, 256, ctypes.byref(_desc(nb=30000)),
                                   ctypes.byref(DecodeOpts(0, 0, 0, 0)), ctypes.byref(plan))
     assert st == 4, st

@@ -297,6 +297,40 @@ def test_fast_group_size_16(hq, hkv, B, oracle_impl):
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
 
 
+SPLIT_DIM_CASES = [(64, 8, 2, 16), (64, 16, 1, 32), (256, 4, 1, 16), (256, 16, 1, 64), (64, 2, 2, 64), (256, 1, 1, 32)]
+
+
+@pytest.mark.parametrize("d,hq,hkv,B", SPLIT_DIM_CASES)
+def test_fast_head_dims_64_256(d, hq, hkv, B, oracle_impl):
+    """bf16 head dims 64 and 256 run on the split-run kernel (one query row per sequence; lanes move
+    two 128-byte rows per load at d = 64, two columns of every row at d = 256).  Lengths at tile and
+    block edges, an empty sequence and past 4k, at several wave counts; one token gives its value
+    row exactly; bad contents poison only their rows; block size 8 stays on the generic kernel."""
+    lengths = [0, 1, 2, 15, 16, 17, 31, 32, 33, 64, 255, 257, 1000, 2048, 4099]
+    w = make_custom(lengths, hq, hkv, d, B, torch.bfloat16, seed=400 + d + B + hq, pool_fill=0.7)
+    assert pkv.PKV_KERNEL_FAST in _kernels_for(w)
+    G = hq // hkv
+    for waves in (0, 1, 3, 64):
+        out = _check_step(w, oracle_impl, f"d{d}/Hq{hq}/Hkv{hkv}/B{B}/waves{waves}", grid_waves=waves)
+        info = pkv.last_launch_info()
+        assert info["kernel"] == "fast" and info["xcd_balance"] == 64, info
+        assert waves == 0 or info["grid"] == waves, info
+        o = out.cpu()
+        assert torch.equal(o[0], torch.zeros_like(o[0]))
+        for h in range(hq):
+            assert torch.equal(o[1, h], w.v_new[1, h // G].float()), (waves, h)
+    bad = make_custom([40, 40, 40, 40], hq, hkv, d, B, torch.bfloat16, seed=62 + d + B)
+    bad.block_tables[1, 1 if B < 40 else 0] = bad.num_blocks + 1000
+    bad.block_tables[2, 0] = -7
+    bad.context_lens[3] = bad.max_blocks_per_seq * B + 1
+    _, out = run_step(bad)
+    o = out.cpu()
+    assert torch.isfinite(o[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
+    w8 = make_custom([1, 17, 300], hq, hkv, d, 8, torch.bfloat16, seed=5)
+    assert pkv.PKV_KERNEL_FAST not in _kernels_for(w8)
+
+
 def test_block_size_8_tile_halves(oracle_impl):
     """Block size 8: every 16-token tile of the fast kernel reads two blocks.  Lengths at and around
     the half-tile and tile edges match the oracle; a table entry past a sequence's tokens is never
