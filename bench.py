@@ -58,6 +58,8 @@ def parse_args(argv=None):
     p.add_argument("--flush-mib", type=int, default=512)
     p.add_argument("--block-size", type=int, default=0,
                    help="redraw the workload's lengths into blocks of this many tokens (block-size sweep)")
+    p.add_argument("--heads", default="",
+                   help="Hq,Hkv,d: the same batch with another head layout (e.g. 128,8,128 or 32,8,256)")
     p.add_argument("--prefix", action="store_true",
                    help="decode with paged_attn_decode_prefix (workloads whose sequences share prefix blocks): "
                         "each shared block is read once per group")
@@ -554,7 +556,8 @@ def main(argv=None) -> int:
 
     dev = torch.device("cuda", 0)
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
-    w = make_config(args.config, block_size=args.block_size or None)
+    heads = tuple(int(x) for x in args.heads.split(",")) if args.heads else None
+    w = make_config(args.config, block_size=args.block_size or None, heads=heads)
     d = {
         "q": w.q.to(dev), "k_new": w.k_new.to(dev), "v_new": w.v_new.to(dev),
         "k_cache": w.k_cache.to(dev), "v_cache": w.v_cache.to(dev),
@@ -621,7 +624,8 @@ def main(argv=None) -> int:
     achieved = moved / (dec_avg * 1e-3) / 1e9
     kv_gbs = nbytes["kv"] / (dec_avg * 1e-3) / 1e9
 
-    key = f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}" + (f"/B{w.block_size}" if args.block_size else "")
+    key = (f"{args.config}/{plan['kernel']}/T{plan['partition_tokens']}" + (f"/B{w.block_size}" if args.block_size else "")
+           + (f"/H{w.num_q_heads}-{w.num_kv_heads}-{w.head_dim}" if heads else ""))
     traffic = _traffic_for(args, key)
 
     rec = {
@@ -712,7 +716,7 @@ def main(argv=None) -> int:
         import oracle
         from workloads import make_config as _mk
 
-        fresh = _mk(args.config, block_size=args.block_size or None)  # pre-write state; the pool was rewritten K+W times (same slots)
+        fresh = _mk(args.config, block_size=args.block_size or None, heads=heads)  # pre-write state; the pool was rewritten K+W times (same slots)
         ref = oracle.decode_step(fresh)
         g = out.double().cpu().numpy()
         err = np.abs(g - ref.out)

@@ -226,7 +226,8 @@ def _build(
 
 
 def make_config(name: str, poison: bool = True, num_seqs: Optional[int] = None,
-                values: bool = True, block_size: Optional[int] = None) -> Workload:
+                values: bool = True, block_size: Optional[int] = None,
+                heads: Optional[Tuple[int, int, int]] = None) -> Workload:
     """One of the five named workloads.
 
     ``num_seqs`` trims the batch (used only to draw a bounded sample of a
@@ -235,6 +236,8 @@ def make_config(name: str, poison: bool = True, num_seqs: Optional[int] = None,
     ``block_size`` redraws the same lengths into blocks of that many tokens (the
     block-size sweep); the table width is scaled to keep the same token
     capacity, and shared prefixes must stay whole blocks.
+    ``heads`` = (query heads, KV heads, head dim) replaces the workload's head
+    layout over the same lengths and tables (other shapes of the same batch).
     """
     seed = _SEEDS[name]
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -271,6 +274,9 @@ def make_config(name: str, poison: bool = True, num_seqs: Optional[int] = None,
         meta = {"lengths": "2048 shared + uniform [1,512]", "prompts": prompts, "samples": samples}
     else:
         raise KeyError(name)
+    if heads is not None:
+        kw["num_q_heads"], kw["num_kv_heads"], kw["head_dim"] = (int(x) for x in heads)
+        meta = dict(meta, heads=f"{kw['num_q_heads']}/{kw['num_kv_heads']}/{kw['head_dim']}")
     if block_size is not None and block_size != kw["block_size"]:
         cap = kw["max_blocks_per_seq"] * kw["block_size"]
         kw["block_size"] = block_size
