@@ -1940,7 +1940,9 @@ __global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a,
 }
 
 // Several new tokens per sequence with all of a KV head's rows in one 16-row
-// block (q_len * G <= 16: the verification of a few drafted tokens).  The
+// block (q_len * G <= 16: the verification of a few drafted tokens), and decode
+// of the shapes decode_fast_kernel does not hold (one row per head: 16 query
+// heads per KV head, head dims 64 and 256).  The
 // tiles of all (sequence, KV head) units are laid end to end, as in
 // decode_fast_kernel, and split into equal runs over the resident waves, so a
 // wave's share does not depend on the length mix.  A wave walks its run in
