@@ -234,7 +234,11 @@ pkv_status paged_attn_decode(const void *q, const void *k_cache, const void *v_c
  *
  * Arguments as paged_attn_decode without workspace and workspace_bytes.  A
  * call whose plan (paged_attn_plan) needs a workspace larger than
- * PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_TOO_LARGE and enqueues nothing.
+ * PKV_NOALLOC_SCRATCH_BYTES runs the generic kernel instead when opts leaves
+ * the kernel to the library (PKV_KERNEL_AUTO) and that plan fits (the
+ * split-run shapes of PKV_KERNEL_FAST size 16 rows for every one of up to
+ * PKV_MAX_GRID_WAVES partial slots); otherwise it returns PKV_ERR_TOO_LARGE
+ * and enqueues nothing.
  * Nothing in the array needs clearing: every byte a call reads was written
  * earlier in that call.  All calls on one GPU share its array, so calls that
  * may overlap on one GPU (two streams, two threads) race: serialise them.

@@ -314,7 +314,16 @@ PKV_API pkv_status paged_attn_decode_noalloc(const void* q, const void* k_cache,
     if (num_seqs == 0) return PKV_OK;
     st = check_decode(q, k_cache, v_cache, block_tables, context_lens, out);
     if (st != PKV_OK) return st;
-    if (plan.workspace_bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_TOO_LARGE;
+    pkv_decode_opts generic = opts ? *opts : pkv_decode_opts{0, PKV_KERNEL_AUTO, 0, 0};
+    if (plan.workspace_bytes > PKV_NOALLOC_SCRATCH_BYTES) {
+        // The library's choice does not fit the array: the generic kernel, if it does.
+        if (generic.kernel != PKV_KERNEL_AUTO || plan.kernel != PKV_KERNEL_FAST) return PKV_ERR_TOO_LARGE;
+        generic.kernel = PKV_KERNEL_GENERIC;
+        if (make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, &generic, &plan) != PKV_OK ||
+            plan.workspace_bytes > PKV_NOALLOC_SCRATCH_BYTES)
+            return PKV_ERR_TOO_LARGE;
+        opts = &generic;
+    }
     void* ws = nullptr;
     if (plan.workspace_bytes > 0) {
         st = scratch_address(&ws);
