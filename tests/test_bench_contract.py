@@ -66,3 +66,17 @@ def test_source_stamp_ignores_comments_and_layout(tmp_path):
     sa, sb, sc = (bench._kernel_source_sha(str(d)) for d in (a, b, c))
     assert sa == sb and sa != sc
     assert len(np.unique([sa, sc])) == 2
+
+
+def test_heads_override_keeps_the_batch():
+    """bench --heads reruns a workload's batch with another head layout: the same lengths, tables and
+    slots, the new head counts and dim, and bytes priced on the new layout."""
+    from workloads import make_config
+
+    base = make_config("llama8b_b64", values=False)
+    other = make_config("llama8b_b64", values=False, heads=(128, 8, 256))
+    assert (other.num_q_heads, other.num_kv_heads, other.head_dim) == (128, 8, 256)
+    assert np.array_equal(base.context_lens, other.context_lens)
+    assert np.array_equal(base.block_tables, other.block_tables)
+    assert np.array_equal(base.slot_mapping, other.slot_mapping)
+    assert bench.algorithmic_bytes(other)["kv"] == 2 * bench.algorithmic_bytes(base)["kv"]
