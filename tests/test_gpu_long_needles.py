@@ -32,7 +32,6 @@ from workloads import make_custom
 pytestmark = pytest.mark.gpu
 
 S, HQ, HKV, D, B, N = 8, 32, 8, 128, 16, 32768
-G = HQ // HKV
 TILES = N // TOK  # tiles per (sequence, KV head) unit
 BIG = 20.0
 
@@ -78,8 +77,14 @@ def _positions(unit, boundaries, extra, rng):
     return sorted(pos)
 
 
+def _shape(w):
+    """(query heads per KV head, block size) of a workload."""
+    return w.q.shape[1] // w.k_cache.shape[1], w.block_size
+
+
 def _plant(w, positions_by_unit):
     """Needles for head g*G + j at positions[j::G] of unit (i, g); returns {(i, h): positions}."""
+    G, _ = _shape(w)
     planted = {}
     for (i, g), plist in positions_by_unit.items():
         for j in range(G):
@@ -96,6 +101,7 @@ def _plant(w, positions_by_unit):
 
 
 def _kv_row(w, which, i, g, p):
+    _, B = _shape(w)
     n = int(w.context_lens[i])
     if p == n - 1:
         return (w.k_new if which == "k" else w.v_new)[i, g].double()
@@ -107,7 +113,7 @@ def _needle_mix(w, i, h, plist):
     """Closed form of head h of sequence i: the softmax mix of its needles' value rows (each
     needle's score from the stored bf16 key and q, in fp64); the other tokens' weight is
     below 1e-4 of it and is left out."""
-    g = h // G
+    g = h // _shape(w)[0]
     q = w.q[i, h].double()
     scores = [w.scale * float(_kv_row(w, "k", i, g, p) @ q) for p in plist]
     assert min(scores) > BIG - 1.0

@@ -63,6 +63,25 @@ def test_config_step(name, oracle_impl):
         _check_step(w, oracle_impl, f"{name}/kernel{k}", kernel=k)
 
 
+HEADS = [(128, 8, 128), (32, 8, 64), (32, 8, 256)]  # (query heads, KV heads, head dim)
+
+
+@pytest.mark.parametrize("heads", HEADS, ids=[f"G{q // k}-d{d}" for q, k, d in HEADS])
+def test_config_step_heads(heads, oracle_impl):
+    """The 64-sequence workload at full size with other head shapes (the batch's lengths and
+    tables as they are): the fast plan runs the split-run kernel; write bit-exact, decode within
+    tolerance on both kernel families."""
+    w = make_config("llama8b_b64", heads=heads)
+    assert (w.num_q_heads, w.num_kv_heads, w.head_dim) == heads
+    assert _kernels_for(w) == [pkv.PKV_KERNEL_GENERIC, pkv.PKV_KERNEL_FAST]
+    for k in (pkv.PKV_KERNEL_FAST, pkv.PKV_KERNEL_GENERIC):
+        _check_step(w, oracle_impl, f"llama8b_b64/H{heads}/kernel{k}", kernel=k)
+        info = pkv.last_launch_info()
+        assert info["kernel"] == ("fast" if k == pkv.PKV_KERNEL_FAST else "generic")
+        if k == pkv.PKV_KERNEL_FAST:  # the split-run kernel: equal runs, K streamed through LDS
+            assert info["xcd_balance"] == 64 and info["k_stream"], info
+
+
 @pytest.mark.parametrize("waves", [1, 3, 8, 64, 1000, 8192])
 def test_fast_wave_count_sweep(waves, oracle_impl):
     """The fast kernel's split points move with the wave count; results stay within tolerance."""
