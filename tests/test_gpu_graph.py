@@ -26,18 +26,26 @@ def _step(d, w, out, ws, kernel):
                           out=out, workspace=ws, kernel=kernel)
 
 
-@pytest.mark.parametrize("kernel", [pkv.PKV_KERNEL_FAST, pkv.PKV_KERNEL_GENERIC])
-def test_decode_step_replays_in_a_graph(kernel, oracle_impl):
+CASES = [  # (kernel, (query heads, KV heads, head dim)); the last two run the split-run decode kernel
+    (pkv.PKV_KERNEL_FAST, (32, 8, 128)),
+    (pkv.PKV_KERNEL_GENERIC, (32, 8, 128)),
+    (pkv.PKV_KERNEL_FAST, (128, 8, 128)),
+    (pkv.PKV_KERNEL_FAST, (32, 8, 256)),
+]
+
+
+@pytest.mark.parametrize("kernel,heads", CASES, ids=[f"k{k}-{q}-{h}-{d}" for k, (q, h, d) in CASES])
+def test_decode_step_replays_in_a_graph(kernel, heads, oracle_impl):
     rng = np.random.Generator(np.random.PCG64(91))
     lengths = rng.integers(1, 1500, size=48, endpoint=True).tolist()
-    w = make_custom(lengths, 32, 8, 128, 16, torch.bfloat16, seed=91, pool_fill=0.8)
+    w = make_custom(lengths, *heads, 16, torch.bfloat16, seed=91, pool_fill=0.8)
     dev = torch.device("cuda", 0)
     d = to_device(w, dev)
     plan = pkv.paged_attn_plan(w.num_seqs, w.num_q_heads, w.max_blocks_per_seq, pkv.cache_desc(d["k_cache"]),
                                kernel=kernel)
     ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    say(f"[gpu] graph kernel={kernel}: S={w.num_seqs} workspace={plan['workspace_bytes']}")
+    say(f"[gpu] graph kernel={kernel} heads={heads}: S={w.num_seqs} workspace={plan['workspace_bytes']}")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
