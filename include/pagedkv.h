@@ -381,9 +381,9 @@ pkv_status paged_attn_decode_multi(const void *q, const void *k_cache, const voi
  *   partition_tokens  fast: 16 (tokens per tile); generic: tokens per partition
  *   k_stream          fast: 1 when K rows were read with non-temporal loads
  *                     (the units were few and long, at most 1/16 of the
- *                     resident waves, the prefix path's suffix pass, group
- *                     size 16, or head dim 64 or 256), 0 when
- *                     with ordinary loads; V rows are always streamed; 0 generic
+ *                     resident waves, the prefix path's suffix pass, or head
+ *                     dim 256), 0 when with ordinary loads; V rows are always
+ *                     streamed; 0 generic
  * Per thread and per process; NULL info gives PKV_ERR_NULL.  For callers that
  * check or report the path taken (for example a benchmark).
  */

@@ -1955,7 +1955,8 @@ __global__ __launch_bounds__(64 * G) void multi_merge_kernel(const DecodeArgs a,
 // from it to the one holding the unit's last tile) for multi_sk_merge_kernel.
 // HD: the head dim (128 on the multi-query path; 64 and 256 for decode).
 // DEC: decode, one query row per sequence (row i of sequence i; cu_q unused).
-template <int BS, int G, int HD, bool DEC>
+// KNT: K rows read with non-temporal loads (V rows always are).
+template <int BS, int G, int HD, bool DEC, bool KNT = true>
 __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float qscale) {
     static_assert(HD == 64 || HD == 128 || HD == 256, "head dim");
     // Tile loads: a token row of K or V is HD / 2 dwords.  Lane l moves dword
@@ -2082,12 +2083,16 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
             }
             __syncthreads();
 
+            auto load_k = [](const uint32_t* p) -> uint32_t {
+                if constexpr (KNT) return load_stream(p);
+                else return *p;
+            };
             auto load_tile = [&](int j, TileKV& tk) {
                 const uint2 o = toff_lds[j];
                 if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
                     const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
 #pragma unroll
-                    for (int k = 0; k < kTok; ++k) tk.k[0][k] = load_stream(k32 + off + k * (kHd / 2));
+                    for (int k = 0; k < kTok; ++k) tk.k[0][k] = load_k(k32 + off + k * (kHd / 2));
 #pragma unroll
                     for (int k = 0; k < kTok; ++k) tk.v[0][k] = load_stream(v32 + off + k * (kHd / 2));
                 } else {
@@ -2095,7 +2100,7 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
 #pragma unroll
-                        for (int k = 0; k < TPL; ++k) tk.k[c][k] = load_stream(k32 + off + k * NC + c * kWave);
+                        for (int k = 0; k < TPL; ++k) tk.k[c][k] = load_k(k32 + off + k * NC + c * kWave);
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
 #pragma unroll
@@ -2493,15 +2498,31 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
     b.total_q = a.num_seqs;
     b.max_q_len = 1;
     const void* k = reinterpret_cast<const void*>(&multi_sk_kernel<BS, G, HD, true>);
-    const int waves = a.grid_waves > 0 ? a.grid_waves : resident_waves(k);
+    const int resident = resident_waves(k);
+    const int waves = a.grid_waves > 0 ? a.grid_waves : resident;
     if (waves <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((multi_sk_kernel<BS, G, HD, true>), dim3(waves), dim3(kWave), 0, stream, b, b.scale * kLog2e);
+    // K rows streamed as in decode_fast_kernel when the units are few (at most a
+    // sixteenth as many as resident waves), and always at head dim 256; else
+    // ordinary loads.  Same box, alternating (streamed against ordinary): 64
+    // sequences of U[128, 4096] at 128/8 heads 108.5-109.3 against 102.1-102.2
+    // us, at 32/2 38.1 against 36.5, at 32/8 heads of 64 dims 54.7 against 52.5,
+    // at 32/8 heads of 256 dims 186.7 against 194.5; 8 x 32k at 128/8 175.1
+    // against 177.9; 256 lognormal lengths at 128/8 337.7 against 339.8.
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+    const bool knt = HD == 256 || units * 16 <= resident;
+    if (knt) {
+        hipLaunchKernelGGL((multi_sk_kernel<BS, G, HD, true, true>), dim3(waves), dim3(kWave), 0, stream, b,
+                           b.scale * kLog2e);
+    } else {
+        hipLaunchKernelGGL((multi_sk_kernel<BS, G, HD, true, false>), dim3(waves), dim3(kWave), 0, stream, b,
+                           b.scale * kLog2e);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid((unsigned)a.num_seqs, 1u, (unsigned)a.num_kv_heads);
     hipLaunchKernelGGL((multi_sk_merge_kernel<G, HD, true>), mgrid, dim3(kWave * G), 0, stream, b, a.max_blocks_per_seq * BS);
     e = hipGetLastError();
-    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, 64, kTok, 1};
+    if (e == hipSuccess) last_launch() = LaunchInfo{PKV_KERNEL_FAST, waves, 64, kTok, knt ? 1 : 0};
     return e;
 }
 

@@ -79,7 +79,9 @@ def test_config_step_heads(heads, oracle_impl):
         info = pkv.last_launch_info()
         assert info["kernel"] == ("fast" if k == pkv.PKV_KERNEL_FAST else "generic")
         if k == pkv.PKV_KERNEL_FAST:  # the split-run kernel: equal runs, K streamed through LDS
-            assert info["xcd_balance"] == 64 and info["k_stream"], info
+            # K streamed when the units are few (at most a sixteenth of the resident waves) or d = 256
+            assert info["xcd_balance"] == 64, info
+            assert info["k_stream"] == (heads[2] == 256 or w.num_seqs * heads[1] * 16 <= info["grid"]), info
 
 
 @pytest.mark.parametrize("waves", [1, 3, 8, 64, 1000, 8192])
@@ -286,7 +288,13 @@ def test_bad_device_contents_stay_in_bounds():
             assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
 
 
-G16_CASES = [(32, 2, 16), (64, 4, 32), (16, 1, 64)]  # (Hq, Hkv, B): 16 query heads per KV head
+G16_CASES = [(32, 2, 16), (64, 4, 32), (16, 1, 64), (128, 8, 16)]  # (Hq, Hkv, B): 16 query heads per KV head
+
+
+def _split_k_stream(info, resident, units, d):
+    """The split-run decode streams K when the units are few (at most a sixteenth of the resident
+    waves) and at head dim 256, else it reads K with ordinary loads."""
+    assert info["k_stream"] == (d == 256 or units * 16 <= resident), (info, resident, units, d)
 
 
 @pytest.mark.parametrize("hq,hkv,B", G16_CASES)
@@ -297,10 +305,13 @@ def test_fast_group_size_16(hq, hkv, B, oracle_impl):
     and 64 waves; one token gives its value row exactly; bad contents poison only their rows."""
     lengths = [0, 1, 2, 15, 16, 17, 31, 32, 33, 64, 255, 257, 1000, 2048, 4099]
     w = make_custom(lengths, hq, hkv, 128, B, torch.bfloat16, seed=300 + B + hq, pool_fill=0.7)
+    resident = 0
     for waves in (0, 1, 3, 64):
         out = _check_step(w, oracle_impl, f"g16/Hq{hq}/Hkv{hkv}/B{B}/waves{waves}", grid_waves=waves)
         info = pkv.last_launch_info()
-        assert info["kernel"] == "fast" and info["xcd_balance"] == 64 and info["k_stream"], info
+        assert info["kernel"] == "fast" and info["xcd_balance"] == 64, info
+        resident = resident or info["grid"]
+        _split_k_stream(info, resident, len(lengths) * hkv, 128)
         assert waves == 0 or info["grid"] == waves, info
         o = out.cpu()
         assert torch.equal(o[0], torch.zeros_like(o[0]))
@@ -316,7 +327,8 @@ def test_fast_group_size_16(hq, hkv, B, oracle_impl):
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
 
 
-SPLIT_DIM_CASES = [(64, 8, 2, 16), (64, 16, 1, 32), (256, 4, 1, 16), (256, 16, 1, 64), (64, 2, 2, 64), (256, 1, 1, 32)]
+SPLIT_DIM_CASES = [(64, 8, 2, 16), (64, 16, 1, 32), (256, 4, 1, 16), (256, 16, 1, 64), (64, 2, 2, 64), (256, 1, 1, 32),
+                   (64, 64, 32, 16)]
 
 
 @pytest.mark.parametrize("d,hq,hkv,B", SPLIT_DIM_CASES)
@@ -329,10 +341,13 @@ def test_fast_head_dims_64_256(d, hq, hkv, B, oracle_impl):
     w = make_custom(lengths, hq, hkv, d, B, torch.bfloat16, seed=400 + d + B + hq, pool_fill=0.7)
     assert pkv.PKV_KERNEL_FAST in _kernels_for(w)
     G = hq // hkv
+    resident = 0
     for waves in (0, 1, 3, 64):
         out = _check_step(w, oracle_impl, f"d{d}/Hq{hq}/Hkv{hkv}/B{B}/waves{waves}", grid_waves=waves)
         info = pkv.last_launch_info()
         assert info["kernel"] == "fast" and info["xcd_balance"] == 64, info
+        resident = resident or info["grid"]
+        _split_k_stream(info, resident, len(lengths) * hkv, d)
         assert waves == 0 or info["grid"] == waves, info
         o = out.cpu()
         assert torch.equal(o[0], torch.zeros_like(o[0]))
