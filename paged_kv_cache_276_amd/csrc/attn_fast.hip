@@ -1962,6 +1962,10 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
     // Tile loads: a token row of K or V is HD / 2 dwords.  Lane l moves dword
     // column(s) l % NCL (+ 64) of TPL tokens, tokens TPL (l / NCL) .. + TPL - 1:
     // each load instruction reads whole rows (HD = 64: two 128-byte rows).
+    // Decode at HD = 128 loads 16-byte pieces instead (lane l: dims 8 (l % 16)
+    // .. + 7 of tokens 4 (l / 16) .. + 3, four whole rows per instruction, a
+    // quarter of the load instructions): 128/8 heads over 64 sequences of
+    // U[128, 4096] 101.0 against 102.5 us, same box, alternating.
     constexpr int NC = HD / 2;                // dword columns of a row
     constexpr int NCL = NC < kWave ? NC : kWave;
     constexpr int CPL = NC / NCL;             // columns per lane: 1, or 2 at HD = 256
@@ -2089,7 +2093,23 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
             };
             auto load_tile = [&](int j, TileKV& tk) {
                 const uint2 o = toff_lds[j];
-                if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
+                if constexpr (HD == kHd && DEC) {
+                    // lane l: 16 bytes (dims 8 (l % 16) .. + 7) of tokens 4 (l / 16) .. + 3,
+                    // one token per load: each load instruction reads 4 whole rows
+                    const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) + (lane >> 4) * 4 * kHd + (lane & 15) * 8;
+                    const uint16_t* k16 = static_cast<const uint16_t*>(a.k_cache);
+                    const uint16_t* v16 = static_cast<const uint16_t*>(a.v_cache);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint4 x = KNT ? load_stream(k16 + off + k * kHd) : *reinterpret_cast<const uint4*>(k16 + off + k * kHd);
+                        tk.k[0][4 * k] = x.x; tk.k[0][4 * k + 1] = x.y; tk.k[0][4 * k + 2] = x.z; tk.k[0][4 * k + 3] = x.w;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint4 x = load_stream(v16 + off + k * kHd);
+                        tk.v[0][4 * k] = x.x; tk.v[0][4 * k + 1] = x.y; tk.v[0][4 * k + 2] = x.z; tk.v[0][4 * k + 3] = x.w;
+                    }
+                } else if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
                     const int64_t off = (int64_t)(((uint64_t)o.y << 32) | o.x) / 2 + lane;
 #pragma unroll
                     for (int k = 0; k < kTok; ++k) tk.k[0][k] = load_k(k32 + off + k * (kHd / 2));
@@ -2111,7 +2131,30 @@ __global__ __launch_bounds__(64) void multi_sk_kernel(const DecodeArgs a, float 
             // context stored as zeros (0 * whatever the slot holds must not
             // reach the sums; the key rows there only give masked scores).
             auto store_tile = [&](int buf, const TileKV& tk, int j) {
-                if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
+                if constexpr (HD == kHd && DEC) {  // tokens 4 tg .. + 3, dims 8 c .. + 7 of this lane
+                    const int tg = lane >> 4, c = lane & 15;
+                    unsigned char* kb = &k_lds[buf][4 * tg * KROW + 16 * c];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        *reinterpret_cast<uint4*>(kb + k * KROW) =
+                            make_uint4(tk.k[0][4 * k], tk.k[0][4 * k + 1], tk.k[0][4 * k + 2], tk.k[0][4 * k + 3]);
+                    const int tokb = (t0 + j) * kTok + 4 * tg;
+                    uint32_t v[kTok];  // v[4 k + q]: dims 8 c + 2 q, + 1 of token 4 tg + k
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[4 * k + q] = tokb + k < ctx ? tk.v[0][4 * k + q] : 0u;
+                    unsigned char* vb = &vt_lds[buf][0];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t t0v = v[q], t1v = v[4 + q], t2v = v[8 + q], t3v = v[12 + q];
+                        const uint2 even = make_uint2((t0v & 0xffffu) | (t1v << 16), (t2v & 0xffffu) | (t3v << 16));
+                        const uint2 odd = make_uint2((t0v >> 16) | (t1v & 0xffff0000u), (t2v >> 16) | (t3v & 0xffff0000u));
+                        *reinterpret_cast<uint2*>(vb + vt_off(8 * c + 2 * q, tg)) = even;
+                        *reinterpret_cast<uint2*>(vb + vt_off(8 * c + 2 * q + 1, tg)) = odd;
+                    }
+                    return;
+                } else if constexpr (HD == kHd) {  // lane l: column l of all 16 tokens
                     unsigned char* kb = &k_lds[buf][4 * lane];
 #pragma unroll
                     for (int k = 0; k < kTok; ++k) *reinterpret_cast<uint32_t*>(kb + k * KROW) = tk.k[0][k];
